@@ -1,0 +1,275 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Every test here runs on the CPU.  None of them derives its expected value from
+the oracle's own code: see tests/_independent.py for the sources used.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import workloads
+from tests import _independent as ind
+
+
+# ---------------------------------------------------------------- decoding
+
+def test_e2m1_matches_printed_table(oracle_lib):
+    table = ind.e2m1_table()
+    for code in range(16):
+        got = oracle_lib.e2m1(code)
+        assert got == table[code], code
+        assert math.copysign(1.0, got) == math.copysign(1.0, table[code]), code
+
+
+def test_e4m3_closed_form_points(oracle_lib):
+    # OCP OFP8 E4M3: bias 7, subnormal step 2^-9, max finite 448, S.1111.111 NaN.
+    assert oracle_lib.e4m3(0x00) == 0.0
+    assert oracle_lib.e4m3(0x01) == 2.0 ** -9
+    assert oracle_lib.e4m3(0x07) == 7 * 2.0 ** -9
+    assert oracle_lib.e4m3(0x08) == 2.0 ** -6
+    assert oracle_lib.e4m3(0x38) == 1.0
+    assert oracle_lib.e4m3(0x3C) == 1.5
+    assert oracle_lib.e4m3(0x7E) == 448.0
+    assert math.isnan(oracle_lib.e4m3(0x7F))
+    assert math.isnan(oracle_lib.e4m3(0xFF))
+
+
+def test_e4m3_sign_symmetry_and_order(oracle_lib):
+    pos = [oracle_lib.e4m3(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+    for c in range(0x7F):
+        assert oracle_lib.e4m3(c | 0x80) == -pos[c]
+
+
+def test_e4m3_matches_library_on_all_codes(oracle_lib):
+    lib = ind.e4m3_table()
+    for c in range(256):
+        got = oracle_lib.e4m3(c)
+        if math.isnan(lib[c]):
+            assert math.isnan(got), c
+        else:
+            assert got == lib[c], c
+
+
+# ---------------------------------------------------------------- rounding
+
+def _np_f16_bits(x: float) -> int:
+    return int(np.array([x], dtype=np.float64).astype(np.float16).view(np.uint16)[0])
+
+
+def test_round_f16_all_values_midpoints_and_neighbours(oracle_lib):
+    """Every positive finite fp16 value h, the midpoint to the next value and
+    one 2^-20 unit either side of it, where those are multiples of 2^-20,
+    rounded by the oracle and by numpy's float64 -> float16 conversion."""
+    hs = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.append(hs[1:], 65536.0)          # 65536 = first value past max
+    checked = 0
+    for h, n in zip(hs, nxt):
+        for x in (h, (h + n) / 2):
+            X = x * 2.0 ** 20
+            if X != math.floor(X):
+                continue
+            for d in (-1, 0, 1):
+                Xi = int(X) + d
+                v = Xi * 2.0 ** -20
+                for s in ((1, -1) if Xi else (1,)):   # exact zero rounds to +0
+                    assert oracle_lib.round_f16_fixed20(s * Xi) == _np_f16_bits(s * v), (s * Xi)
+                checked += 1
+    assert checked > 60000
+
+
+def test_round_f16_overflow_boundary(oracle_lib):
+    u = 2 ** 20
+    assert oracle_lib.round_f16_fixed20(65504 * u) == 0x7BFF
+    assert oracle_lib.round_f16_fixed20(65520 * u - 1) == 0x7BFF
+    assert oracle_lib.round_f16_fixed20(65520 * u) == 0x7C00        # tie -> even -> inf
+    assert oracle_lib.round_f16_fixed20(-65520 * u) == 0xFC00
+    assert oracle_lib.round_f16_fixed20(2 ** 62) == 0x7C00
+    assert oracle_lib.round_f16_fixed20(0) == 0x0000
+    assert oracle_lib.round_f16_fixed20(1) == 0x0010               # 2^-20 = 16 * 2^-24
+
+
+def test_round_f16_random_vs_numpy(oracle_lib):
+    rng = np.random.default_rng(7)
+    for mag in (2 ** 10, 2 ** 24, 2 ** 34, 2 ** 40):
+        for X in rng.integers(-mag, mag, size=3000):
+            X = int(X)
+            assert oracle_lib.round_f16_fixed20(X) == _np_f16_bits(X * 2.0 ** -20), X
+
+
+# ------------------------------------------------------- structure and values
+
+def _onehot_case(M, N, K, m, n, k, ca, cb, sa_code, sb_code):
+    A = np.zeros((M, K), np.uint8)
+    B = np.zeros((N, K), np.uint8)
+    A[m, k] = ca
+    B[n, k] = cb
+    # distinct scales on every block, the chosen one on block k // 16
+    SFA = np.full((M, K // 16), 0x30, np.uint8)
+    SFB = np.full((N, K // 16), 0x40, np.uint8)
+    SFA[:, :] = (0x30 + np.arange(K // 16)) % 0x70 + 1
+    SFB[:, :] = (0x48 + 3 * np.arange(K // 16)) % 0x70 + 1
+    SFA[m, k // 16] = sa_code
+    SFB[n, k // 16] = sb_code
+    return ind.pack_fp4(A), ind.pack_fp4(B), SFA, SFB
+
+
+@pytest.mark.parametrize("k", [0, 1, 14, 15, 16, 17, 30, 31, 63])
+def test_onehot_nibble_order_and_scale_index(oracle_lib, k):
+    M, N, K = 3, 5, 64
+    m, n = 2, 3
+    t = ind.e2m1_table()
+    s = ind.e4m3_table()
+    ca, cb, sa, sb = 7, 13, 0x3D, 0x2A     # 6.0, -3.0, 1.625, 0.3125
+    A, B, SFA, SFB = _onehot_case(M, N, K, m, n, k, ca, cb, sa, sb)
+    C, X = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SFA], [SFB], exact=True)
+    want = t[ca] * s[sa] * t[cb] * s[sb]
+    expect = np.zeros((M, N))
+    expect[m, n] = want
+    np.testing.assert_array_equal(X[0], expect)
+    assert C[0].view(np.uint16)[m, n] == _np_f16_bits(want)
+    assert np.count_nonzero(C[0].astype(np.float64)) == 1
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 16), (3, 5, 32), (8, 7, 64), (4, 8, 48)])
+def test_bruteforce_unit_scales(oracle_lib, shape):
+    M, N, K = shape
+    key = workloads.stream_key(99, M, N, K)
+    A = workloads.random_bytes(key, M * K // 2).reshape(M, K // 2)
+    B = workloads.random_bytes(key + np.uint64(1), N * K // 2).reshape(N, K // 2)
+    SFA = np.full((M, K // 16), 0x38, np.uint8)
+    SFB = np.full((N, K // 16), 0x38, np.uint8)
+    want16, want = ind.brute_group(A, B, SFA, SFB, M, N, K)
+    C, X = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SFA], [SFB], exact=True)
+    np.testing.assert_array_equal(X[0], want)
+    np.testing.assert_array_equal(C[0].view(np.uint16), want16.view(np.uint16))
+
+
+@pytest.mark.parametrize("dist", ["pos", "finite"])
+@pytest.mark.parametrize("shape", [(5, 6, 64), (8, 8, 64), (2, 9, 16)])
+def test_bruteforce_random_scales(oracle_lib, dist, shape):
+    """Float64 sums are exact here: every product is a multiple of 2^-20 below
+    2^23 and K <= 64, so partial sums stay below 2^29 (49 bits)."""
+    M, N, K = shape
+    A, B, SFA, SFB = workloads.make_group(5, 0, M, N, K, dist=dist)
+    want16, want = ind.brute_group(A, B, SFA, SFB, M, N, K)
+    C, X = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SFA], [SFB], exact=True)
+    np.testing.assert_array_equal(X[0], want)
+    got = C[0].view(np.uint16)
+    w = want16.view(np.uint16)
+    zero = want == 0                       # the sign of an exact zero is not pinned
+    np.testing.assert_array_equal(got[~zero], w[~zero])
+    assert np.all(C[0][zero] == 0)
+
+
+def test_int64_and_f64_paths_agree_on_config_inputs(oracle_lib):
+    cfg = workloads.CONFIGS[0]
+    A, B, SA, SB = workloads.config_inputs(cfg)
+    C1, X1 = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB, exact=True)
+    C2, X2 = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB,
+                                   exact=True, use_f64=True)
+    for i in range(cfg["g"]):
+        np.testing.assert_array_equal(X1[i], X2[i])
+        np.testing.assert_array_equal(C1[i].view(np.uint16), C2[i].view(np.uint16))
+
+
+def test_config1_matches_bruteforce(oracle_lib):
+    """The whole small workload against float64 matmul: products are multiples
+    of 2^-14 below 2^13, K = 512, so sums stay below 2^22 / 2^-14 = 2^36."""
+    cfg = workloads.CONFIGS[0]
+    A, B, SA, SB = workloads.config_inputs(cfg)
+    C = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB)
+    for i in range(cfg["g"]):
+        w16, _ = ind.brute_group(A[i], B[i], SA[i], SB[i], cfg["M"][i], cfg["N"][i], cfg["K"][i])
+        np.testing.assert_array_equal(C[i].view(np.uint16), w16.view(np.uint16))
+
+
+def test_group_independence(oracle_lib):
+    M, N, K = [16, 8, 24], [32, 16, 8], [64, 128, 32]
+    A, B, SA, SB = workloads.make_inputs(M, N, K, 3)
+    C = oracle_lib.group_gemm(M, N, K, A, B, SA, SB)
+    A2 = list(A)
+    A2[1] = A[1] ^ np.uint8(0x5A)
+    C2 = oracle_lib.group_gemm(M, N, K, A2, B, SA, SB)
+    for i in (0, 2):
+        np.testing.assert_array_equal(C[i].view(np.uint16), C2[i].view(np.uint16))
+    assert not np.array_equal(C[1].view(np.uint16), C2[1].view(np.uint16))
+    for i in range(3):
+        Ci = oracle_lib.group_gemm([M[i]], [N[i]], [K[i]], [A[i]], [B[i]], [SA[i]], [SB[i]])
+        np.testing.assert_array_equal(Ci[0].view(np.uint16), C[i].view(np.uint16))
+
+
+def test_transpose_symmetry(oracle_lib):
+    M, N, K = 12, 20, 96
+    A, B, SA, SB = workloads.make_group(8, 0, M, N, K, dist="finite")
+    C = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SA], [SB])[0]
+    Ct = oracle_lib.group_gemm([N], [M], [K], [B], [A], [SB], [SA])[0]
+    np.testing.assert_array_equal(C.view(np.uint16), Ct.T.view(np.uint16))
+
+
+def test_element_matches_full(oracle_lib):
+    M, N, K = 7, 9, 160
+    A, B, SA, SB = workloads.make_group(4, 1, M, N, K)
+    C, X = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SA], [SB], exact=True)
+    for m in range(M):
+        for n in range(N):
+            c16, ex = oracle_lib.gemm_element(M, N, K, A, B, SA, SB, m, n)
+            assert c16 == int(C[0].view(np.uint16)[m, n])
+            assert ex == X[0][m, n]
+
+
+def test_dequant_matches_independent_decode(oracle_lib):
+    rows, K = 256, 32
+    X = ind.pack_fp4(np.tile(np.arange(16, dtype=np.uint8), (rows, K // 16)))
+    SF = np.repeat(np.arange(256, dtype=np.uint8)[:, None], K // 16, axis=1)
+    got = oracle_lib.dequant(X, SF, rows, K)
+    want = ind.decode(X, SF, rows, K)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok], want[ok])
+
+
+def test_nan_scale_gives_nan(oracle_lib):
+    """Reading taken where the pages are silent: a NaN scale code used by an
+    output makes that output NaN (IEEE: NaN times anything is NaN)."""
+    M, N, K = 2, 3, 32
+    A, B, SA, SB = workloads.make_group(1, 0, M, N, K)
+    SA = SA.copy()
+    SA[1, 1] = 0x7F
+    C = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SA], [SB])[0]
+    assert not np.isnan(C[0].astype(np.float32)).any()
+    assert np.isnan(C[1].astype(np.float32)).all()
+
+
+def test_degenerate_sizes(oracle_lib):
+    C = oracle_lib.group_gemm([0, 3], [4, 0], [32, 32],
+                              [np.zeros(0, np.uint8), np.zeros(48, np.uint8)],
+                              [np.zeros(64, np.uint8), np.zeros(0, np.uint8)],
+                              [np.zeros(0, np.uint8), np.zeros(6, np.uint8)],
+                              [np.zeros(8, np.uint8), np.zeros(0, np.uint8)])
+    assert C[0].shape == (0, 4) and C[1].shape == (3, 0)
+    # K = 0: empty sums are exactly zero
+    C = oracle_lib.group_gemm([2], [2], [0], [np.zeros(0, np.uint8)], [np.zeros(0, np.uint8)],
+                              [np.zeros(0, np.uint8)], [np.zeros(0, np.uint8)])
+    assert np.all(C[0].view(np.uint16) == 0)
+
+
+# ------------------------------------------- sensitivity of the pins above
+
+def test_pins_detect_plausible_mistakes(oracle_lib):
+    """The brute-force pin would catch an oracle that swapped the nibble order,
+    transposed B, or indexed scales per 32 instead of 16: each such change
+    alters the expected values on these inputs."""
+    M, N, K = 4, 4, 64
+    A, B, SA, SB = workloads.make_group(11, 0, M, N, K)
+    base16, base = ind.brute_group(A, B, SA, SB, M, N, K)
+    swapped = ((A >> 4) | (A << 4)).astype(np.uint8)
+    assert not np.array_equal(ind.brute_group(swapped, B, SA, SB, M, N, K)[1], base)
+    assert not np.array_equal(ind.brute_group(A, B.reshape(N, K // 2)[::-1].copy(), SA, SB, M, N, K)[1], base)
+    SA32 = np.repeat(SA[:, ::2], 2, axis=1)
+    assert not np.array_equal(ind.brute_group(A, B, SA32, SB, M, N, K)[1], base)
+    C = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SA], [SB])[0]
+    np.testing.assert_array_equal(C.view(np.uint16), base16.view(np.uint16))
