@@ -1,0 +1,90 @@
+/*
+ * nvfp4gg.h -- C ABI of the MI355X (gfx950) NVFP4 block-scaled grouped GEMM.
+ *
+ * The operation (kernelindex page kernelbot-nvfp4-group-gemm-444497, header
+ * comment of its kernel source; page kernelbot-nvfp4-group-gemm-505431,
+ * custom_kernel_fallback and apply_scale_factors): for every group i,
+ *
+ *   C_i[m][n] = sum_k a_i(m,k) * sfa_i(m, k/16) * b_i(n,k) * sfb_i(n, k/16)
+ *
+ * rounded to fp16 (round-to-nearest-even, overflow to +-inf), accumulated in
+ * fp32.  a, b are FP4 E2M1 codes, sfa, sfb are FP8 E4M3 scales, one per 16
+ * consecutive K of a row.
+ *
+ * Memory layouts (all row-major, unpadded):
+ *   A_i   M_i x K_i   FP4, two codes per byte, row stride K_i/2 bytes; element
+ *                     2j of a row is the low nibble of byte j, element 2j+1 the
+ *                     high nibble (page 505431, dequantize_fp4).
+ *   B_i   N_i x K_i   same as A_i.
+ *   SFA_i M_i x K_i/16 E4M3 bytes, scale of A_i[m][16s .. 16s+15] at [m][s]
+ *                     (page 505431, apply_scale_factors: plain [rows, K/16]).
+ *   SFB_i N_i x K_i/16 likewise for B_i.
+ *   C_i   M_i x N_i   fp16, row stride N_i elements (page 505431, the epilogue
+ *                     of group_gemm_kernel_impl addresses C as row * N + col).
+ *
+ * Ownership: the caller allocates and owns every buffer.  The size arrays and
+ * the pointer arrays are HOST memory, read only during the call; each element
+ * pointer is a DEVICE pointer.  C_i is overwritten.  The library keeps no
+ * state between calls apart from the thread-local error message.
+ *
+ * Streams: work is enqueued on `stream` (a hipStream_t; NULL is the default
+ * stream) and the call returns without synchronising.
+ *
+ * Errors: every argument is validated before any HIP call.  Return codes:
+ *   NVFP4GG_OK            0  success (also when every group is empty)
+ *   NVFP4GG_INVALID_ARG  -1  g <= 0, a NULL array, a negative size, K_i not a
+ *                            multiple of 16, a NULL or misaligned (16-byte)
+ *                            device pointer of a non-empty operand
+ *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle (an
+ *                            operand above 2 GiB; see nvfp4_group_gemm)
+ *   NVFP4GG_HIP_ERROR    -3  a HIP launch failed
+ * nvfp4_group_gemm_last_error() describes the last failure on this thread.
+ */
+#ifndef NVFP4GG_H
+#define NVFP4GG_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4GG_OK 0
+#define NVFP4GG_INVALID_ARG (-1)
+#define NVFP4GG_UNSUPPORTED (-2)
+#define NVFP4GG_HIP_ERROR (-3)
+
+/* Grouped GEMM, one pass over all groups.
+ *   g                 number of groups (>= 1; any count, groups are launched
+ *                     in batches that fit the kernel-argument block)
+ *   M, N, K           host arrays of g sizes; M_i, N_i >= 0 (a group with
+ *                     M_i == 0 or N_i == 0 is skipped), K_i >= 0, K_i % 16 == 0
+ *                     (K_i == 0 writes zeros to C_i)
+ *   A_ptrs .. SFB_ptrs host arrays of g device pointers to the packed operands
+ *   C_ptrs            host array of g device pointers to the fp16 outputs
+ *   stream            hipStream_t (NULL: default stream)
+ */
+int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
+                     const void* const* A_ptrs, const void* const* B_ptrs,
+                     const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                     void* const* C_ptrs, void* stream);
+
+/* The dequantisation step alone, with the same device code the GEMM uses:
+ * out[r][k] = fp16( e2m1(X[r][k]) * e4m3(SFX[r][k/16]) ) for a rows x K
+ * packed FP4 matrix X and its rows x K/16 scales (layouts as A_i, SFA_i
+ * above; page 505431, dequantize_fp4 and apply_scale_factors).  out is a
+ * device buffer of rows*K fp16, row-major.  The product of an E2M1 and an
+ * E4M3 value has at most 6 significant bits and lies within fp16's normal
+ * range, so the result is exact.  Same return codes as nvfp4_group_gemm. */
+int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
+                      void* out, void* stream);
+
+/* Thread-local description of the last non-OK return ("" if none). */
+const char* nvfp4_group_gemm_last_error(void);
+
+/* ABI version of this header: 1. */
+int nvfp4_group_gemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4GG_H */
