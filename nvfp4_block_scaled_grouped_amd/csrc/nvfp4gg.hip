@@ -7,71 +7,98 @@
 // declared in include/nvfp4gg.h.
 //
 // Design (gfx950 first; the pages' Blackwell kernels are prior art only):
-//   * Scale resolution: every A and B element is dequantised in registers to
-//     fp16 as e2m1(code) * e4m3(scale).  That product has at most 6
-//     significant bits and lies in [2^-10, 2688], so fp16 holds it exactly,
-//     and the fp16 x fp16 products inside the MFMA are exact in fp32.  The
-//     contraction then runs on v_mfma_f32_16x16x32_f16 with fp32 accumulation.
-//     (CDNA4's block-scaled f8f6f4 MFMA takes power-of-two E8M0 scales per 32
-//     K; it cannot carry an E4M3 mantissa per 16 K, and no 8-bit operand
-//     format holds a 6-bit significand.)
+//   * Scale resolution: every A and B element is dequantised to fp16 as
+//     e2m1(code) * e4m3(scale).  That product has at most 6 significant bits
+//     and lies in [2^-10, 2688], so fp16 holds it exactly, and the fp16 x fp16
+//     products inside the MFMA are exact in fp32.  The contraction runs on
+//     v_mfma_f32_32x32x16_f16 with fp32 accumulation.  (CDNA4's block-scaled
+//     f8f6f4 MFMA takes power-of-two E8M0 scales per 32 K; it cannot carry an
+//     E4M3 mantissa per 16 K, and no 8-bit operand format holds a 6-bit
+//     significand.)
 //   * Dequant: v_cvt_scalef32_pk_f16_fp4 turns two FP4 codes into two fp16
-//     (scale operand 1.0), then v_pk_mul_f16 multiplies by the E4M3 scale
-//     converted to fp16 (exact: E4M3 is a subset of fp16).
-//   * K order: the sum over K is order-free, so each 16-lane group q of a
-//     wave owns a contiguous quarter of every 256-wide K step (32 bytes per
-//     row = two 16-byte loads, one 4-byte scale load).  In MFMA k-step j the
-//     lane feeds the 8 codes of dword j of its quarter; A and B use the same
-//     assignment, so the pairs (a_k, b_k) meet in the same MFMA slot.
-//   * Accumulation is hierarchical: each 512-K stretch accumulates into a
-//     fresh fp32 tile that is then added into the running tile, which keeps
-//     the rounding error of long K sums small next to outputs near zero.
-//   * Loads are raw buffer loads with the exact byte size as the range, so
+//     (its scale operand contributes only a power of two, so it is passed
+//     1.0), then v_pk_mul_f16 multiplies by the E4M3 scale converted to fp16
+//     (exact: every E4M3 value is an fp16 value).
+//   * Tile: one workgroup of 8 waves per CU owns up to 128 rows of A_i
+//     (1..4 fragments of 32 rows) x 256 columns of B_i; wave w owns columns
+//     [32w, 32w+32) of the tile for all its rows.  A is shared: each 256-K
+//     stage of the tile's A rows is dequantised once by the workgroup into
+//     LDS as fp16, already in MFMA operand order, and every wave reads it with
+//     16-byte LDS loads.  B is private to a wave: each lane loads its own MFMA
+//     operand bytes (a full 128-byte line per row per stage) straight into
+//     registers and dequantises them there, so one dequantised B fragment
+//     feeds up to 4 MFMAs.
+//   * K order: the sum over K is order-free.  Within a 256-K stage, lane half
+//     h (lanes 32h..32h+31) owns K [128h, 128h+128) and feeds, in MFMA k-step
+//     j, the 8 codes of dword j of that range.  A and B use the same
+//     assignment, so every pair (a_k, b_k) meets in the same MFMA slot.
+//   * Accumulation is hierarchical: each stretch of at most 2048 K
+//     accumulates into a fresh fp32 tile that is then added into the running
+//     tile, which keeps the rounding error of long K sums small next to
+//     outputs near zero.
+//   * Schedule: the work is the list of (tile, stage) units (schedule.h); a
+//     persistent grid of one workgroup per CU takes equal-cost contiguous
+//     ranges of it, so ragged groups fill the chip in one launch.  A tile
+//     whose stages span several workgroups is finished by the last of them
+//     to arrive: each writes its fp32 partial tile to a workspace slot and
+//     bumps the tile's counter; the one that sees all others done sums the
+//     partials in workgroup order (deterministic) and writes C.  No
+//     workgroup ever waits for another.
+//   * Loads are raw buffer loads whose range is the exact operand size, so
 //     rows past M_i or N_i read as zero without branches.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "nvfp4gg.h"
+#include "schedule.h"
 
 namespace {
+
+using namespace nvfp4sched;
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef float f16x_t __attribute__((ext_vector_type(16)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = kWave * kWavesPerBlock;
-constexpr int kBM = 64;                       // rows of A per block (4 x 16)
-constexpr int kWN = 64;                       // columns of B per wave (4 x 16)
-constexpr int kBN = kWN * kWavesPerBlock;     // columns of B per block
-constexpr int kKStep = 256;                   // K per pipeline step
-constexpr int kFlushSteps = 2;                // K steps per partial accumulation
-constexpr int kMaxGroupsPerLaunch = 32;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWave * kWaves;
+constexpr int kKSteps = kStageK / 16;        // MFMA k-steps per stage (16 K each: 8 per lane half)
+constexpr int kFlushStages = 8;              // stages per partial accumulation (2048 K)
+constexpr int kSlotFloats = kWaves * kMaxFrags * kWave * 16;   // one partial tile
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
+constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
 
-struct GroupDesc {
+static_assert(kTileN == kWaves * 32, "one 32-column fragment per wave");
+
+struct GroupArgs {
     const uint8_t* A;
     const uint8_t* B;
     const uint8_t* SFA;
     const uint8_t* SFB;
     uint16_t* C;
     int M, N, K;
-    int item_begin;   // first work item of this group within the launch
-    int mblocks;      // ceil(M / kBM)
-    int nblocks;      // ceil(N / kBN)
-    int pad0, pad1;
+    int pad;
 };
 
 struct LaunchArgs {
-    GroupDesc g[kMaxGroupsPerLaunch];
+    GroupSched sched[kMaxGroups];
+    GroupArgs grp[kMaxGroups];
+    float* partials;      // G * 2 slots of kSlotFloats
+    int* counters;        // one per tile, zero between calls
+    int64_t W;            // total cost
+    int G;                // workgroups
     int ngroups;
-    int total_items;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
@@ -91,181 +118,300 @@ __device__ __forceinline__ h8_t dequant8(uint32_t packed, _Float16 s)
     return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// One 16-row operand fragment for one 256-wide K step, as one lane holds it:
-// 32 bytes of codes (8 dwords, 64 consecutive K) and their 4 scale bytes.
-struct Frag {
-    i4_t lo, hi;
-    uint32_t sc;
-};
-
-__device__ __forceinline__ Frag load_frag(__amdgpu_buffer_rsrc_t codes, __amdgpu_buffer_rsrc_t scales,
-                                          uint32_t code_off, uint32_t scale_off)
+// Four E4M3 scale bytes of a dword -> fp16.
+__device__ __forceinline__ void scales4(uint32_t sc, _Float16* out)
 {
-    Frag f;
-    f.lo = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(codes, code_off, 0, 0));
-    f.hi = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(codes, code_off + 16, 0, 0));
-    f.sc = __builtin_amdgcn_raw_buffer_load_b32(scales, scale_off, 0, 0);
-    return f;
-}
-
-__device__ __forceinline__ uint32_t frag_dword(const Frag& f, int j)
-{
-    return (uint32_t)(j < 4 ? f.lo[j & 3] : f.hi[j & 3]);
-}
-
-// Scales of k-steps (0,1), (2,3), (4,5), (6,7) are bytes 0..3 of f.sc.
-__device__ __forceinline__ void frag_scales(const Frag& f, _Float16 out[4])
-{
-    const h2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sc, 1.0f, false);
-    const h2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(f.sc, 1.0f, true);
+    const h2_t s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+    const h2_t s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
     out[0] = s01.x;
     out[1] = s01.y;
     out[2] = s23.x;
     out[3] = s23.y;
 }
 
-__global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
+__device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    const int item = blockIdx.x;
-    int gi = 0;
-    for (int i = 1; i < args.ngroups; ++i)
-        if (item >= args.g[i].item_begin) gi = i;
-    const GroupDesc& G = args.g[gi];
+    return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
-    const int li = item - G.item_begin;
-    const int mb = li % G.mblocks;
-    const int nb = li / G.mblocks;
-    const int wave = threadIdx.x / kWave;
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+// LDS image of the dequantised A rows of one stage, in MFMA operand order:
+// [fragment][k-step][lane] x 8 fp16 (64 KB).
+struct AStage {
+    h8_t v[kMaxFrags][kKSteps][kWave];
+};
+
+// fp16 round-to-nearest-even (overflow to inf) of 4 floats, packed.
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d)
+{
+    uint2 w;
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)c) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)d) << 16);
+    return w;
+}
+
+// Store the fp32 tile held in acc to C.  acc[fm] element r of lane (l32, h)
+// of wave w is C[m0 + 32 fm + l32][ncol + 8 (r / 4) + 4 h + r % 4], where
+// ncol is the wave's first column.
+template <int MF>
+__device__ __forceinline__ void store_c(const GroupArgs& ga, int m0, int ncol, const f16x_t* acc)
+{
     const int lane = threadIdx.x % kWave;
-    const int r16 = lane & 15;   // row within a 16-row fragment
-    const int q = lane >> 4;     // K quarter owned by this lane group
-
-    const int M = G.M, N = G.N, K = G.K;
-    const int m0 = mb * kBM;
-    const int n0 = nb * kBN + wave * kWN;
-    const uint32_t row_bytes = (uint32_t)K / 2;
-    const uint32_t row_scales = (uint32_t)K / 16;
-
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(G.A, (uint32_t)M * row_bytes);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(G.B, (uint32_t)N * row_bytes);
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(G.SFA, (uint32_t)M * row_scales);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(G.SFB, (uint32_t)N * row_scales);
-
-    uint32_t offA[4], offSA[4], offB[4], offSB[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        const uint32_t ra = (uint32_t)(m0 + 16 * f + r16);
-        const uint32_t rb = (uint32_t)(n0 + 16 * f + r16);
-        offA[f] = ra * row_bytes + 32u * q;
-        offSA[f] = ra * row_scales + 4u * q;
-        offB[f] = rb * row_bytes + 32u * q;
-        offSB[f] = rb * row_scales + 4u * q;
-    }
-
-    // acc[i][j]: output tile with B fragment i (16 columns of C) as the MFMA
-    // A operand and A fragment j (16 rows of C) as the MFMA B operand.
-    f4_t acc[4][4];
-    f4_t part[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            acc[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-            part[i][j] = f4_t{0.f, 0.f, 0.f, 0.f};
-        }
-
-    Frag fa[4], fb[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        fa[f] = load_frag(rA, rSA, offA[f], offSA[f]);
-        fb[f] = load_frag(rB, rSB, offB[f], offSB[f]);
-    }
-
-    int step = 0;
-    for (int kb = 0; kb < K; kb += kKStep, ++step) {
-        // Prefetch the next step (range-checked loads; unused past K).
-        Frag na[4], nbf[4];
-        const uint32_t nk_bytes = (uint32_t)(kb + kKStep) / 2;
-        const uint32_t nk_scales = (uint32_t)(kb + kKStep) / 16;
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            na[f] = load_frag(rA, rSA, offA[f] + nk_bytes, offSA[f] + nk_scales);
-            nbf[f] = load_frag(rB, rSB, offB[f] + nk_bytes, offSB[f] + nk_scales);
-        }
-
-        _Float16 sa[4][4], sb[4][4];
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            frag_scales(fa[f], sa[f]);
-            frag_scales(fb[f], sb[f]);
-        }
-
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            h8_t av[4], bv[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                av[f] = dequant8(frag_dword(fa[f], j), sa[f][j >> 1]);
-                bv[f] = dequant8(frag_dword(fb[f], j), sb[f][j >> 1]);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    part[i][jj] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[i], av[jj], part[i][jj], 0, 0, 0);
-        }
-
-        if ((step % kFlushSteps) == kFlushSteps - 1 || kb + kKStep >= K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    acc[i][jj] += part[i][jj];
-                    part[i][jj] = f4_t{0.f, 0.f, 0.f, 0.f};
-                }
-        }
-
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            fa[f] = na[f];
-            fb[f] = nbf[f];
-        }
-    }
-
-    // Epilogue: lane holds C[m][n .. n+3] for m = m0 + 16 jj + r16,
-    // n = n0 + 16 i + 4 q; fp32 -> fp16 round-to-nearest-even (overflow to inf).
-    uint16_t* C = G.C;
+    const int l32 = lane & 31, h = lane >> 5;
+    const int M = ga.M, N = ga.N;
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-        const int m = m0 + 16 * jj + r16;
+    for (int fm = 0; fm < MF; ++fm) {
+        const int m = m0 + 32 * fm + l32;
         if (m >= M) continue;
+        uint16_t* row = ga.C + (size_t)m * N;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = n0 + 16 * i + 4 * q;
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int n = ncol + 8 * q4 + 4 * h;
             if (n >= N) continue;
-            const f4_t v = acc[i][jj];
-            const _Float16 h[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
-            uint16_t* dst = C + (size_t)m * N + n;
+            const f16x_t& v = acc[fm];
+            const uint2 w = pack4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
             if (vec_ok && n + 3 < N) {
-                uint2 w;
-                w.x = (uint32_t)__builtin_bit_cast(uint16_t, h[0]) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, h[1]) << 16);
-                w.y = (uint32_t)__builtin_bit_cast(uint16_t, h[2]) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, h[3]) << 16);
-                *reinterpret_cast<uint2*>(dst) = w;
+                *reinterpret_cast<uint2*>(row + n) = w;
             } else {
-                for (int e = 0; e < 4 && n + e < N; ++e)
-                    dst[e] = __builtin_bit_cast(uint16_t, h[e]);
+                const uint16_t o[4] = {(uint16_t)(w.x & 0xFFFF), (uint16_t)(w.x >> 16),
+                                       (uint16_t)(w.y & 0xFFFF), (uint16_t)(w.y >> 16)};
+                for (int e = 0; e < 4 && n + e < N; ++e) row[n + e] = o[e];
             }
         }
     }
 }
 
-// Dequantisation alone, through the same fragment path as the GEMM: one
-// thread per 64 consecutive codes of a row (one quarter-step of a lane),
-// i.e. 8 dwords of codes and the 4 scale bytes that cover them.  Blocks past
-// the end of the row are skipped.
+// One segment [s_begin, s_end) of the stages of a tile with MF fragments.
+template <int MF>
+__device__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end, AStage* As,
+                            int* s_flag)
+{
+    const GroupSched& gs = args.sched[pos.group];
+    const GroupArgs& ga = args.grp[pos.group];
+    const int wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    const int l32 = lane & 31;
+    const int h = lane >> 5;
+    const int M = ga.M, N = ga.N, K = ga.K;
+    const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
+    const int ncol = pos.nb * kTileN + wave * 32;
+    const uint32_t row_bytes = (uint32_t)K / 2;
+    const uint32_t row_scales = (uint32_t)K / 16;
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
+
+    // B operand of lane (l32, h): row ncol + l32, bytes [64h, 64h+64) and
+    // scale bytes [8h, 8h+8) of each stage.
+    const uint32_t brow = (uint32_t)(ncol + l32);
+    const uint32_t offB = brow * row_bytes + 64u * h;
+    const uint32_t offSB = brow * row_scales + 8u * h;
+    // A loader: thread (r5, ah, af, ap) reads row m0 + 32 af + r5, bytes
+    // [64 ah + 32 ap, +32) and scale bytes [8 ah + 4 ap, +4) of each stage and
+    // writes k-steps 8 ap .. 8 ap + 7 of lane r5 + 32 ah of fragment af.
+    const int r5 = threadIdx.x & 31;
+    const int ah = (threadIdx.x >> 5) & 1;
+    const int af = (threadIdx.x >> 6) & 3;
+    const int ap = threadIdx.x >> 8;
+    const bool a_active = af < MF;
+    const uint32_t arow = (uint32_t)(m0 + 32 * af + r5);
+    const uint32_t offA = arow * row_bytes + 64u * ah + 32u * ap;
+    const uint32_t offSA = arow * row_scales + 8u * ah + 4u * ap;
+
+    auto store_a = [&](AStage& dst, const i4_t& c0, const i4_t& c1, uint32_t sc) {
+        _Float16 s[4];
+        scales4(sc, s);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) dst.v[af][8 * ap + t][r5 + 32 * ah] = dequant8((uint32_t)c0[t], s[t >> 1]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            dst.v[af][8 * ap + 4 + t][r5 + 32 * ah] = dequant8((uint32_t)c1[t], s[2 + (t >> 1)]);
+    };
+
+    f16x_t acc[MF], part[MF];
+#pragma unroll
+    for (int f = 0; f < MF; ++f) {
+        acc[f] = f16x_t{};
+        part[f] = f16x_t{};
+    }
+
+    // Prologue: stage s_begin of A into LDS buffer 0 and of B into registers.
+    const uint32_t sb0 = (uint32_t)s_begin * (kStageK / 2);
+    const uint32_t ss0 = (uint32_t)s_begin * (kStageK / 16);
+    if (a_active) store_a(As[0], load16(rA, offA + sb0), load16(rA, offA + sb0 + 16), load4(rSA, offSA + ss0));
+    i4_t b[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b[c] = load16(rB, offB + sb0 + 16 * c);
+    uint32_t bsc0 = load4(rSB, offSB + ss0), bsc1 = load4(rSB, offSB + ss0 + 4);
+    __syncthreads();
+
+    const int n = s_end - s_begin;
+    for (int i = 0; i < n; ++i) {
+        const int buf = i & 1;
+        const bool more = i + 1 < n;
+        const uint32_t nbytes = (uint32_t)(s_begin + i + 1) * (kStageK / 2);
+        const uint32_t nscales = (uint32_t)(s_begin + i + 1) * (kStageK / 16);
+        // A of the next stage (dequantised into the other buffer at the end).
+        i4_t na0 = i4_t{}, na1 = i4_t{};
+        uint32_t nasc = 0;
+        if (a_active && more) {
+            na0 = load16(rA, offA + nbytes);
+            na1 = load16(rA, offA + nbytes + 16);
+            nasc = load4(rSA, offSA + nscales);
+        }
+        _Float16 sb[8];
+        scales4(bsc0, sb);
+        scales4(bsc1, sb + 4);
+        if (more) {
+            bsc0 = load4(rSB, offSB + nscales);
+            bsc1 = load4(rSB, offSB + nscales + 4);
+        }
+
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = 4 * c + jj;
+                const h8_t bv = dequant8((uint32_t)b[c][jj], sb[j >> 1]);
+#pragma unroll
+                for (int fm = 0; fm < MF; ++fm) {
+                    const h8_t av = As[buf].v[fm][j][lane];
+                    part[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, part[fm], 0, 0, 0);
+                }
+            }
+            // This 16-byte piece of B is consumed: fetch the next stage's.
+            if (more) b[c] = load16(rB, offB + nbytes + 16 * c);
+        }
+
+        if (((i + 1) % kFlushStages) == 0 || !more) {
+#pragma unroll
+            for (int f = 0; f < MF; ++f) {
+                acc[f] += part[f];
+                part[f] = f16x_t{};
+            }
+        }
+
+        if (a_active && more) store_a(As[buf ^ 1], na0, na1, nasc);
+        __syncthreads();
+    }
+
+    // Finish the tile: alone, or as one of several contributors.
+    const int unit = pos.frags + 1;
+    const int64_t c_first = pos.tile_cost0;
+    const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
+    const int w_first = owner(args.W, args.G, c_first);
+    const int w_last = owner(args.W, args.G, c_last);
+    if (w_first == w_last) {
+        store_c<MF>(ga, m0, ncol, acc);
+        return;
+    }
+    const int me = blockIdx.x;
+    const int tile = tile_index(args.sched, pos);
+    // Partial tile -> this workgroup's slot.  The stores carry the
+    // device-scope coherence bit (sc1), so they are written through past
+    // this XCD's L2; waiting for them before the counter update publishes
+    // them to whichever workgroup finishes the tile, with no cache flush.
+    const __amdgpu_buffer_rsrc_t rP = make_rsrc(args.partials, (uint32_t)(2 * args.G) * kSlotFloats * 4u);
+    {
+        const uint32_t slot_off = (uint32_t)(me * 2 + (me < w_last ? 1 : 0)) * kSlotFloats * 4u;
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm) {
+            const uint32_t off = slot_off + (uint32_t)((wave * kMaxFrags + fm) * kWave + lane) * 64u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(i4_t, f4_t{acc[fm][4 * q], acc[fm][4 * q + 1], acc[fm][4 * q + 2],
+                                                  acc[fm][4 * q + 3]}),
+                    rP, off + 16u * q, 0, kCoherent);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old =
+            __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = (old == w_last - w_first) ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = *s_flag != 0;
+    __syncthreads();   // s_flag is reused by the next segment
+    if (!last) return;
+    // Sum every contributor's partial (this workgroup's included) in
+    // workgroup order, so the result does not depend on who arrived last.
+    // The loads carry the device-scope coherence bit as well.
+    for (int w = w_first; w <= w_last; ++w) {
+        const uint32_t slot_off = (uint32_t)(w * 2 + (w < w_last ? 1 : 0)) * kSlotFloats * 4u;
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm) {
+            const uint32_t off = slot_off + (uint32_t)((wave * kMaxFrags + fm) * kWave + lane) * 64u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4_t v = __builtin_bit_cast(
+                    f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, off + 16u * q, 0, kCoherent));
+                if (w == w_first) {
+                    acc[fm][4 * q] = v.x;
+                    acc[fm][4 * q + 1] = v.y;
+                    acc[fm][4 * q + 2] = v.z;
+                    acc[fm][4 * q + 3] = v.w;
+                } else {
+                    acc[fm][4 * q] += v.x;
+                    acc[fm][4 * q + 1] += v.y;
+                    acc[fm][4 * q + 2] += v.z;
+                    acc[fm][4 * q + 3] += v.w;
+                }
+            }
+        }
+    }
+    store_c<MF>(ga, m0, ncol, acc);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
+{
+    __shared__ AStage As[2];
+    __shared__ int s_flag;
+
+    const int w = blockIdx.x;
+    const int64_t b1 = boundary(args.W, args.G, w + 1);
+    Pos pos = locate(args.sched, args.ngroups, boundary(args.W, args.G, w));
+    while (pos.group < args.ngroups && stage_cost(pos, pos.stage) < b1) {
+        const GroupSched& gs = args.sched[pos.group];
+        const int unit = pos.frags + 1;
+        // Stages of this tile that start before b1.
+        const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
+        const int s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
+        switch (pos.frags) {
+            case 1: run_segment<1>(args, pos, pos.stage, s_end, As, &s_flag); break;
+            case 2: run_segment<2>(args, pos, pos.stage, s_end, As, &s_flag); break;
+            case 3: run_segment<3>(args, pos, pos.stage, s_end, As, &s_flag); break;
+            default: run_segment<4>(args, pos, pos.stage, s_end, As, &s_flag); break;
+        }
+        if (s_end < gs.stages) break;
+        pos = locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages);
+    }
+}
+
+// Writes zeros to C of a group with K == 0 (the empty sum).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint16_t* C, int64_t count)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
+         i += (int64_t)gridDim.x * blockDim.x)
+        C[i] = 0;
+}
+
+// Dequantisation alone, with the same conversion code as the GEMM: one
+// thread per 64 consecutive codes of a row (8 dwords) and the 4 scale bytes
+// that cover them.  Blocks past the end of the row are skipped.
 __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(int rows, int K, const uint8_t* X,
                                                             const uint8_t* SFX, h8_t* out)
 {
@@ -277,7 +423,6 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(int rows, int K, con
     const int b0 = (int)(t % quads) * 4;
     const int nb = blocks - b0 < 4 ? blocks - b0 : 4;
 
-    Frag f;
     uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     uint32_t sc = 0;
     const uint32_t* xrow = reinterpret_cast<const uint32_t*>(X + r * (K / 2));
@@ -286,15 +431,12 @@ __global__ __launch_bounds__(256) void nvfp4_dequant_kernel(int rows, int K, con
         w[2 * b + 1] = xrow[2 * (b0 + b) + 1];
         sc |= (uint32_t)SFX[r * blocks + b0 + b] << (8 * b);
     }
-    f.lo = i4_t{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-    f.hi = i4_t{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
-    f.sc = sc;
     _Float16 s[4];
-    frag_scales(f, s);
+    scales4(sc, s);
     h8_t* orow = out + r * (K / 8);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        if (j < 2 * nb) orow[2 * b0 + j] = dequant8(frag_dword(f, j), s[j >> 1]);
+        if (j < 2 * nb) orow[2 * b0 + j] = dequant8(w[j], s[j >> 1]);
 }
 
 thread_local std::string g_last_error;
@@ -308,6 +450,72 @@ int fail(int code, const std::string& msg)
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Minimum cost handed to one workgroup: keeps every workgroup range longer
+// than the costliest stage (kMaxFrags + 1 units), which the fixup relies on.
+constexpr int64_t kMinUnitsPerWG = 16;
+static_assert(kMinUnitsPerWG >= kMaxFrags + 1, "a workgroup range must hold a stage");
+
+// Workspace of the split-tile fixup, one per (device, stream): the partial
+// tiles and the per-tile counters (zero between calls; the last contributor
+// of a tile resets its counter).  Allocated on first use and kept.
+struct Workspace {
+    float* partials = nullptr;
+    size_t slots = 0;
+    int* counters = nullptr;
+    size_t ncounters = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::map<int, int> g_cus;
+
+int get_workspace(int dev, hipStream_t s, int G, int tiles, Workspace& out)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[std::make_pair(dev, (void*)s)];
+    const size_t need_slots = 2 * (size_t)G;
+    if (w.slots < need_slots) {
+        if (w.partials) {
+            if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.partials) != hipSuccess)
+                return fail(NVFP4GG_HIP_ERROR, "workspace release failed");
+            w.partials = nullptr;
+            w.slots = 0;
+        }
+        if (hipMalloc(&w.partials, need_slots * kSlotFloats * sizeof(float)) != hipSuccess) {
+            w.partials = nullptr;
+            return fail(NVFP4GG_HIP_ERROR, "workspace allocation failed");
+        }
+        w.slots = need_slots;
+    }
+    if (w.ncounters < (size_t)tiles) {
+        if (w.counters) {
+            if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.counters) != hipSuccess)
+                return fail(NVFP4GG_HIP_ERROR, "workspace release failed");
+            w.counters = nullptr;
+            w.ncounters = 0;
+        }
+        const size_t n = tiles > 4096 ? (size_t)tiles : 4096;
+        if (hipMalloc(&w.counters, n * sizeof(int)) != hipSuccess ||
+            hipMemset(w.counters, 0, n * sizeof(int)) != hipSuccess) {
+            w.counters = nullptr;
+            return fail(NVFP4GG_HIP_ERROR, "workspace allocation failed");
+        }
+        w.ncounters = n;
+    }
+    out = w;
+    return NVFP4GG_OK;
+}
+
+int device_cus(int dev)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_cus.find(dev);
+    if (it != g_cus.end()) return it->second;
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    g_cus[dev] = v;
+    return v;
+}
 
 }  // namespace
 
@@ -336,42 +544,80 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
         for (const void* p : ops)
             if (!p || !aligned16(p))
                 return fail(NVFP4GG_INVALID_ARG, gs + "an operand pointer is NULL or not 16-byte aligned");
-        if (K[i] % kKStep != 0)
+        if (K[i] % kStageK != 0)
             return fail(NVFP4GG_UNSUPPORTED, gs + "this kernel needs K % 256 == 0");
-        // Byte offsets of the buffer loads are 32-bit and may run one block
+        // Byte offsets of the buffer loads are 32-bit and may run one tile
         // past the last row.
-        const int64_t rows = (int64_t)(M[i] > N[i] ? M[i] : N[i]) + kBN;
+        const int64_t rows = (int64_t)(M[i] > N[i] ? M[i] : N[i]) + kTileN;
         if (rows * (K[i] / 2) >= ((int64_t)1 << 31))
             return fail(NVFP4GG_UNSUPPORTED, gs + "operand larger than 2 GiB");
+        if ((int64_t)M[i] * N[i] >= ((int64_t)1 << 31))
+            return fail(NVFP4GG_UNSUPPORTED, gs + "output larger than 2^31 elements");
     }
 
+    bool any_work = false;
+    for (int i = 0; i < g; ++i) any_work |= (M[i] > 0 && N[i] > 0);
+    if (!any_work) return NVFP4GG_OK;
+
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(NVFP4GG_HIP_ERROR, "hipGetDevice failed");
+    const int cus = device_cus(dev);
+
+    // Groups with K == 0 get C = 0 (the empty sum).
+    for (int i = 0; i < g; ++i) {
+        if (M[i] == 0 || N[i] == 0 || K[i] != 0) continue;
+        const int64_t count = (int64_t)M[i] * N[i];
+        const int blocks = (int)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint16_t*>(C_ptrs[i]),
+                           count);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    }
+
     LaunchArgs args;
     int gi = 0;
     while (gi < g) {
         std::memset(&args, 0, sizeof(args));
-        int items = 0;
         int n = 0;
-        for (; gi < g && n < kMaxGroupsPerLaunch; ++gi) {
-            if (M[gi] == 0 || N[gi] == 0) continue;
-            GroupDesc& d = args.g[n++];
-            d.A = static_cast<const uint8_t*>(A_ptrs[gi]);
-            d.B = static_cast<const uint8_t*>(B_ptrs[gi]);
-            d.SFA = static_cast<const uint8_t*>(SFA_ptrs[gi]);
-            d.SFB = static_cast<const uint8_t*>(SFB_ptrs[gi]);
-            d.C = static_cast<uint16_t*>(C_ptrs[gi]);
-            d.M = M[gi];
-            d.N = N[gi];
-            d.K = K[gi];
-            d.item_begin = items;
-            d.mblocks = ceil_div(M[gi], kBM);
-            d.nblocks = ceil_div(N[gi], kBN);
-            items += d.mblocks * d.nblocks;
+        int tiles = 0;
+        int64_t cost = 0;
+        for (; gi < g && n < kMaxGroups; ++gi) {
+            if (M[gi] == 0 || N[gi] == 0 || K[gi] == 0) continue;
+            GroupSched& sc = args.sched[n];
+            GroupArgs& ga = args.grp[n];
+            ++n;
+            ga.A = static_cast<const uint8_t*>(A_ptrs[gi]);
+            ga.B = static_cast<const uint8_t*>(B_ptrs[gi]);
+            ga.SFA = static_cast<const uint8_t*>(SFA_ptrs[gi]);
+            ga.SFB = static_cast<const uint8_t*>(SFB_ptrs[gi]);
+            ga.C = static_cast<uint16_t*>(C_ptrs[gi]);
+            ga.M = M[gi];
+            ga.N = N[gi];
+            ga.K = K[gi];
+            sc.frags = ceil_div(M[gi], kFragRows);
+            sc.mblocks = ceil_div(sc.frags, kMaxFrags);
+            sc.nblocks = ceil_div(N[gi], kTileN);
+            sc.stages = K[gi] / kStageK;
+            sc.cost_begin = cost;
+            sc.tile_begin = tiles;
+            cost += group_cost(sc);
+            tiles += sc.mblocks * sc.nblocks;
         }
         if (n == 0) continue;
         args.ngroups = n;
-        args.total_items = items;
-        hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(items), dim3(kThreads), 0, s, args);
+        args.W = cost;
+        int64_t G = cost / kMinUnitsPerWG;
+        if (G > cus) G = cus;
+        if (G < 1) G = 1;
+        args.G = (int)G;
+        Workspace ws;
+        const int rc = get_workspace(dev, s, args.G, tiles, ws);
+        if (rc != NVFP4GG_OK) return rc;
+        args.partials = ws.partials;
+        args.counters = ws.counters;
+        hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -390,9 +636,8 @@ extern "C" int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX
     const int64_t total = (int64_t)rows * ((K / 16 + 3) / 4);
     if (total > ((int64_t)1 << 31) - 256) return fail(NVFP4GG_UNSUPPORTED, "too many elements");
     const int nblk = (int)((total + 255) / 256);
-    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(nblk), dim3(256), 0,
-                       reinterpret_cast<hipStream_t>(stream), rows, K,
-                       static_cast<const uint8_t*>(X), static_cast<const uint8_t*>(SFX),
+    hipLaunchKernelGGL(nvfp4_dequant_kernel, dim3(nblk), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       rows, K, static_cast<const uint8_t*>(X), static_cast<const uint8_t*>(SFX),
                        static_cast<h8_t*>(out));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)

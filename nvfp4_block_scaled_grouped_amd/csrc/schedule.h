@@ -1,0 +1,145 @@
+// schedule.h -- work decomposition of the grouped GEMM into (tile, K-stage)
+// units and their even split over a persistent grid (stream-K style).
+//
+// Plain C++ usable from host and device code; the kernel and the host
+// launcher include it, and a CPU test compiles it on its own.
+//
+// Terms:
+//   * fragment: 32 rows of A_i (the MFMA tile height).
+//   * m-block: up to kMaxFrags fragments of one group, processed together.
+//     A group with F = ceil(M/32) fragments has nmb = ceil(F / kMaxFrags)
+//     m-blocks; fragments are spread evenly, so the first F % nmb m-blocks
+//     get F / nmb + 1 fragments and the rest F / nmb.
+//   * n-block: kTileN columns of B_i.
+//   * tile: (group, n-block, m-block); tiles are ordered by group, then
+//     n-block, then m-block, so the m-blocks that share a B strip are
+//     adjacent in the order.
+//   * stage: kStageK consecutive K of a tile.  A stage of a tile with f
+//     fragments costs f + 1 units (MFMA work grows with f; the B work of
+//     the stage does not).
+//   * Workgroup w of G takes the cost range [w*W/G, (w+1)*W/G), rounded up
+//     to stage starts, so every stage belongs to exactly one workgroup.
+#ifndef NVFP4GG_SCHEDULE_H
+#define NVFP4GG_SCHEDULE_H
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define NVFP4_HD __host__ __device__ __forceinline__
+#else
+#define NVFP4_HD inline
+#endif
+
+namespace nvfp4sched {
+
+constexpr int kMaxFrags = 4;       // fragments per m-block
+constexpr int kFragRows = 32;      // rows per fragment
+constexpr int kTileN = 256;        // columns per n-block
+constexpr int kStageK = 256;       // K per stage
+constexpr int kMaxGroups = 32;     // groups per launch
+
+struct GroupSched {
+    int64_t cost_begin;   // cost units before this group
+    int frags;            // ceil(M / 32)
+    int mblocks;          // ceil(frags / kMaxFrags)
+    int nblocks;          // ceil(N / kTileN)
+    int stages;           // K / kStageK
+    int tile_begin;       // tiles before this group
+};
+
+NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Fragments of m-block i of a group with F fragments in nmb m-blocks.
+NVFP4_HD int mblock_frags(int F, int nmb, int i)
+{
+    const int base = F / nmb, extra = F % nmb;
+    return base + (i < extra ? 1 : 0);
+}
+
+// First fragment of m-block i.
+NVFP4_HD int mblock_first_frag(int F, int nmb, int i)
+{
+    const int base = F / nmb, extra = F % nmb;
+    return i * base + (i < extra ? i : extra);
+}
+
+// Cost of one n-block column of a group (all m-blocks, all stages).
+NVFP4_HD int64_t column_cost(const GroupSched& g)
+{
+    return (int64_t)(g.frags + g.mblocks) * g.stages;
+}
+
+NVFP4_HD int64_t group_cost(const GroupSched& g) { return column_cost(g) * g.nblocks; }
+
+// A unit position: tile (group, n-block, m-block) and stage.
+struct Pos {
+    int group, nb, mb, stage;
+    int frags;            // fragments of the m-block
+    int64_t tile_cost0;   // cost position of the tile's stage 0
+};
+
+// The stage-aligned position of cost point p: the first stage that starts at
+// or after p.  Every group must have cost > 0 (the host launches no empty
+// group).  For p >= the total cost the result has group == ngroups.
+NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
+{
+    Pos r;
+    for (;;) {
+        int gi = 0;
+        while (gi + 1 < ngroups && gs[gi + 1].cost_begin <= p) ++gi;
+        const GroupSched& g = gs[gi];
+        int64_t q = p - g.cost_begin;
+        if (q >= group_cost(g)) {
+            r.group = ngroups;
+            r.nb = r.mb = r.stage = r.frags = 0;
+            r.tile_cost0 = p;
+            return r;
+        }
+        const int64_t cc = column_cost(g);
+        r.group = gi;
+        r.nb = (int)(q / cc);
+        q -= (int64_t)r.nb * cc;
+        // Cost before m-block i of a column is (first_frag(i) + i) * stages.
+        int mb = 0;
+        while (mb + 1 < g.mblocks &&
+               (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb + 1) + mb + 1) * g.stages <= q)
+            ++mb;
+        r.mb = mb;
+        r.frags = mblock_frags(g.frags, g.mblocks, mb);
+        const int64_t mcost0 = (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb) + mb) * g.stages;
+        q -= mcost0;
+        const int unit = r.frags + 1;
+        r.stage = (int)((q + unit - 1) / unit);
+        r.tile_cost0 = g.cost_begin + (int64_t)r.nb * cc + mcost0;
+        if (r.stage < g.stages) return r;
+        p = r.tile_cost0 + (int64_t)unit * g.stages;   // rounded past the tile: next tile
+    }
+}
+
+// Cost position of stage s of the tile at position p.
+NVFP4_HD int64_t stage_cost(const Pos& p, int s) { return p.tile_cost0 + (int64_t)s * (p.frags + 1); }
+
+// Workgroup boundary b_w = floor(w * W / G) (w = 0..G).
+NVFP4_HD int64_t boundary(int64_t W, int G, int w) { return (W * (int64_t)w) / G; }
+
+// The workgroup that owns the stage starting at cost position c
+// (the largest w with b_w <= c).
+NVFP4_HD int owner(int64_t W, int G, int64_t c)
+{
+    int64_t w = (c * G + G - 1) / W;
+    if (w > G - 1) w = G - 1;
+    while (w > 0 && boundary(W, G, (int)w) > c) --w;
+    while (w + 1 < G && boundary(W, G, (int)w + 1) <= c) ++w;
+    return (int)w;
+}
+
+// Global tile index of a position.
+NVFP4_HD int tile_index(const GroupSched* gs, const Pos& p)
+{
+    const GroupSched& g = gs[p.group];
+    return g.tile_begin + p.nb * g.mblocks + p.mb;
+}
+
+}  // namespace nvfp4sched
+
+#endif  // NVFP4GG_SCHEDULE_H

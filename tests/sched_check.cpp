@@ -1,0 +1,124 @@
+// CPU check of the work decomposition in schedule.h: replays every
+// workgroup's walk over (tile, stage) units exactly as the kernel does and
+// verifies the partition and the split-tile bookkeeping.
+#include <cstdio>
+#include <cstdlib>
+#include <map>
+#include <random>
+#include <set>
+#include <vector>
+
+#include "../nvfp4_block_scaled_grouped_amd/csrc/schedule.h"
+
+using namespace nvfp4sched;
+
+static int fails = 0;
+#define CHECK(c, ...) do { if (!(c)) { ++fails; std::printf("FAIL %s:%d: ", __FILE__, __LINE__); std::printf(__VA_ARGS__); std::printf("\n"); return; } } while (0)
+
+static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus,
+                     int64_t min_units)
+{
+    int ng = (int)M.size();
+    GroupSched gs[kMaxGroups];
+    int64_t cost = 0;
+    int tiles = 0;
+    for (int i = 0; i < ng; ++i) {
+        gs[i].frags = ceil_div_i(M[i], kFragRows);
+        gs[i].mblocks = ceil_div_i(gs[i].frags, kMaxFrags);
+        gs[i].nblocks = ceil_div_i(N[i], kTileN);
+        gs[i].stages = K[i] / kStageK;
+        gs[i].cost_begin = cost;
+        gs[i].tile_begin = tiles;
+        cost += group_cost(gs[i]);
+        tiles += gs[i].mblocks * gs[i].nblocks;
+        // m-block partition covers all fragments, each block 1..kMaxFrags
+        int sum = 0;
+        for (int b = 0; b < gs[i].mblocks; ++b) {
+            int f = mblock_frags(gs[i].frags, gs[i].mblocks, b);
+            CHECK(f >= 1 && f <= kMaxFrags, "mblock frags %d", f);
+            CHECK(mblock_first_frag(gs[i].frags, gs[i].mblocks, b) == sum, "first frag");
+            sum += f;
+        }
+        CHECK(sum == gs[i].frags, "frag sum");
+    }
+    const int64_t W = cost;
+    int64_t G64 = W / min_units;
+    if (G64 > cus) G64 = cus;
+    if (G64 < 1) G64 = 1;
+    const int G = (int)G64;
+    // covered[(tile, stage)] = workgroup
+    std::map<std::pair<int, int>, int> covered;
+    std::map<int, std::set<int>> contrib;         // tile -> workgroups
+    std::map<std::pair<int, int>, int> slot_use;  // (wg, slot) -> tile
+    for (int w = 0; w < G; ++w) {
+        const int64_t b1 = boundary(W, G, w + 1);
+        Pos pos = locate(gs, ng, boundary(W, G, w));
+        int guard = 0;
+        while (pos.group < ng && stage_cost(pos, pos.stage) < b1) {
+            CHECK(++guard < 1000000, "runaway walk");
+            const GroupSched& g = gs[pos.group];
+            const int unit = pos.frags + 1;
+            const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
+            const int s_end = s_end64 < g.stages ? (int)s_end64 : g.stages;
+            CHECK(s_end > pos.stage, "empty segment w=%d", w);
+            const int t = tile_index(gs, pos);
+            CHECK(t >= 0 && t < tiles, "tile index %d", t);
+            for (int s = pos.stage; s < s_end; ++s) {
+                auto key = std::make_pair(t, s);
+                CHECK(!covered.count(key), "stage covered twice t=%d s=%d", t, s);
+                covered[key] = w;
+                CHECK(owner(W, G, stage_cost(pos, s)) == w, "owner mismatch t=%d s=%d w=%d", t, s, w);
+            }
+            contrib[t].insert(w);
+            const int64_t c_first = pos.tile_cost0;
+            const int64_t c_last = pos.tile_cost0 + (int64_t)(g.stages - 1) * unit;
+            const int wf = owner(W, G, c_first), wl = owner(W, G, c_last);
+            CHECK(wf <= w && w <= wl, "contributor range");
+            if (wf != wl) {
+                const int slot = w < wl ? 1 : 0;
+                auto sk = std::make_pair(w, slot);
+                CHECK(!slot_use.count(sk), "slot reused w=%d slot=%d", w, slot);
+                slot_use[sk] = t;
+                CHECK(w * 2 + slot < 2 * G, "slot bound");
+            }
+            if (s_end < g.stages) break;
+            pos = locate(gs, ng, pos.tile_cost0 + (int64_t)unit * g.stages);
+        }
+    }
+    // every stage of every tile covered exactly once
+    int64_t expect = 0;
+    for (int i = 0; i < ng; ++i) expect += (int64_t)gs[i].mblocks * gs[i].nblocks * gs[i].stages;
+    CHECK((int64_t)covered.size() == expect, "covered %zu of %lld stages", covered.size(), (long long)expect);
+    // contributors of each tile form the contiguous range [owner(first), owner(last)]
+    for (auto& kv : contrib) {
+        const std::set<int>& ws = kv.second;
+        const int lo = *ws.begin(), hi = *ws.rbegin();
+        CHECK((int)ws.size() == hi - lo + 1, "tile %d contributors not contiguous", kv.first);
+    }
+}
+
+int main()
+{
+    // The five workloads.
+    run_case({64, 96}, {256, 256}, {512, 512}, 256, 16);
+    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256, 16);
+    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256, 16);
+    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256, 16);
+    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256, 16);
+    // Random shapes and grid sizes.
+    std::mt19937 rng(12345);
+    for (int it = 0; it < 3000; ++it) {
+        const int ng = 1 + rng() % 12;
+        std::vector<int> M, N, K;
+        for (int i = 0; i < ng; ++i) {
+            M.push_back(1 + rng() % 700);
+            N.push_back(1 + rng() % 3000);
+            K.push_back(256 * (1 + rng() % 12));
+        }
+        run_case(M, N, K, 1 + rng() % 300, 5 + rng() % 40);
+        if (fails) break;
+    }
+    if (fails) { std::printf("FAILED %d\n", fails); return 1; }
+    std::printf("OK\n");
+    return 0;
+}
