@@ -12,12 +12,20 @@ hold it between back-to-back calls, so the timed loop rotates through several
 independent input sets (435 MB for three) and each call reads inputs the
 previous calls did not touch.
 
-Prints ONE JSON line (rank 0) with the metric, µs/call, HBM GB/s and TFLOP/s,
-the roofline of the kernel and the CPU oracle's time on a bounded sample.
+Prints ONE JSON line with the metric, µs/call, HBM GB/s and TFLOP/s, the
+roofline of the kernel and the CPU oracle's time on a bounded sample.
+
+Counter mode: ``python bench.py --traffic-from FETCH_CSV WRITE_CSV`` reads the
+rocprofv3 counter_collection.csv files of a FETCH_SIZE run and a WRITE_SIZE
+run of ``bench.py --calib-copy-mb N`` and prints the HBM traffic per launch of
+the GEMM kernel, each counter scaled by what it reads for the plain device
+copy of known size that the same run performed.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +42,10 @@ import workloads  # noqa: E402
 METRIC = "µs/call + achieved HBM GB/s & TFLOP/s, NVFP4 grouped GEMM g=8 K=7168 N=4096"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+KERNEL = "nvfp4_group_gemm_kernel"
+CALIB_KERNEL = "neg"            # torch.neg's elementwise kernel: reads and writes the copy size
+CSRC = os.path.join(ROOT, "nvfp4_block_scaled_grouped_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def parse():
@@ -44,13 +56,74 @@ def parse():
     ap.add_argument("--config", default=workloads.HEADLINE["name"],
                     help="workload name (default: the g=8 K=7168 N=4096 grouped GEMM)")
     ap.add_argument("--sets", type=int, default=0,
-                    help="input sets rotated through (0: enough to exceed 384 MB)")
+                    help="input sets rotated through (0: enough to exceed 384 MB, at most 64)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="after timing, run one device copy of this many MB (counter calibration)")
+                    help="after timing, run 3 device copies of this many MiB (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the counter-derived traffic per launch and exit (no GPU use)")
     return ap.parse_args()
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources, so stored counter figures are only
+    used for the kernel they were taken on."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, "%s_%s_traffic.txt" % (KERNEL, workload))
+
+
+def read_traffic(workload: str):
+    """Bytes per launch from the stored counter summary, or None when there
+    is none or it was taken on other kernel sources."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#", "|")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def counter_means(path: str):
+    """{kernel name: (dispatches, mean counter value)} of a counter_collection.csv."""
+    acc = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_mb: int):
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        means = counter_means(path)
+        gemm = [v for k, v in means.items() if KERNEL in k]
+        calib = [v for k, v in means.items() if CALIB_KERNEL in k and KERNEL not in k]
+        if len(gemm) != 1 or len(calib) != 1:
+            raise SystemExit("%s: expected one GEMM and one copy kernel, found %s" % (path, list(means)))
+        known_kib = copy_mb * 1024.0
+        factor = known_kib / calib[0][1]
+        out[counter] = dict(gemm_kib=gemm[0][1], gemm_dispatches=gemm[0][0], copy_kib=calib[0][1],
+                            factor=factor, bytes=gemm[0][1] * factor * 1024.0)
+    return out
 
 
 def make_device_sets(cfg, nsets, torch):
@@ -66,38 +139,51 @@ def make_device_sets(cfg, nsets, torch):
 
 
 def cpu_baseline(cfg, target_s):
-    """The oracle, as it is, on the first rows of group 0 (all N, all K),
-    scaled to the whole workload by multiply-add count."""
+    """The oracle, as it is, on the first r_i rows of every group (all N_i
+    columns, all K_i), r_i the same fraction of M_i in each group, grown until
+    the run takes about target_s; scaled to the whole workload by
+    multiply-add count."""
     import oracle
     oracle.build(force=False)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    A, B, SA, SB = workloads.make_group(cfg["seed"], 0, M[0], N[0], K[0])
+    g = len(M)
+    inputs = [workloads.make_group(cfg["seed"], i, M[i], N[i], K[i]) for i in range(g)]
     total_macs = sum(m * n * k for m, n, k in zip(M, N, K))
     threads = oracle.max_threads()
 
-    def run(rows):
+    def run(frac):
+        rows = [max(1, min(M[i], int(round(M[i] * frac)))) for i in range(g)]
+        A = [inputs[i][0][:rows[i]] for i in range(g)]
+        SA = [inputs[i][2][:rows[i]] for i in range(g)]
         t0 = time.perf_counter()
-        oracle.group_gemm([rows], [N[0]], [K[0]], [A[:rows]], [B], [SA[:rows]], [SB],
+        oracle.group_gemm(rows, N, K, A, [x[1] for x in inputs], SA, [x[3] for x in inputs],
                           nthreads=threads)
-        return time.perf_counter() - t0
+        return rows, time.perf_counter() - t0
 
-    rows = max(1, min(M[0], threads))
-    t = run(rows)
-    while t < target_s / 4 and rows < M[0]:
-        rows = min(M[0], rows * 2)
-        t = run(rows)
-    if t < target_s and rows < M[0]:
-        rows = min(M[0], max(rows, int(rows * target_s / max(t, 1e-3))))
-        t = run(rows)
-    macs = rows * N[0] * K[0]
+    frac = min(1.0, threads / max(1.0, sum(M)))
+    rows, t = run(frac)
+    while t < target_s / 4 and frac < 1.0:
+        frac = min(1.0, frac * 2)
+        rows, t = run(frac)
+    if t < target_s * 0.7 and frac < 1.0:
+        frac = min(1.0, frac * target_s / max(t, 1e-3))
+        rows, t = run(frac)
+    macs = sum(r * n * k for r, n, k in zip(rows, N, K))
     us_per_call = t * 1e6 * total_macs / macs
-    return {"value": us_per_call, "unit": "µs/call", "cores": threads, "kind": "oracle",
-            "sample": "group 0 rows 0..%d (all %d columns, K=%d): %d of %d multiply-adds, %.1f s, "
-                      "scaled to the whole workload" % (rows - 1, N[0], K[0], macs, total_macs, t)}
+    return {"value": round(us_per_call, 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
+            "sample": "first rows %s of the %d groups (all N, all K): %d of %d multiply-adds in %.1f s "
+                      "on %d threads, scaled to the whole workload" % (rows, g, macs, total_macs, t, threads)}
 
 
 def main():
     args = parse()
+    if args.traffic_from:
+        mb = args.calib_copy_mb or 512
+        t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb)
+        total = int(round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]))
+        print(json.dumps({"source_sha256": source_digest(), "calib_copy_mb": mb, "counters": t,
+                          "traffic_bytes_per_launch": total}, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
               "(the grouped GEMM would shard whole groups or N-slices across GPUs with no "
@@ -111,23 +197,24 @@ def main():
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     abytes = workloads.algorithmic_bytes(M, N, K)
     flops = workloads.algorithmic_flops(M, N, K)
-    nsets = args.sets or max(1, -(-384 * 2 ** 20 // abytes))
+    nsets = args.sets or min(64, max(1, -(-384 * 2 ** 20 // abytes)))
     sets = make_device_sets(cfg, nsets, torch)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    ptrs = [dict(A=[t.data_ptr() for t in s["A"]], B=[t.data_ptr() for t in s["B"]],
-                 SA=[t.data_ptr() for t in s["SA"]], SB=[t.data_ptr() for t in s["SB"]],
-                 C=[t.data_ptr() for t in s["C"]]) for s in sets]
+    calls = [nv.GroupGemmCall(M, N, K, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
+                              [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
+                              [t.data_ptr() for t in s["C"]], sh) for s in sets]
 
     def step(i):
-        p = ptrs[i % nsets]
-        rc = nv.group_gemm_ptrs(M, N, K, p["A"], p["B"], p["SA"], p["SB"], p["C"], sh)
+        rc = calls[i % nsets]()
         if rc != nv.OK:
             raise RuntimeError(nv.last_error())
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # Events on the stream the kernel is launched on, one between every two
+    # calls: the mean gap is the kernel's average duration in the loop.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)
@@ -140,13 +227,16 @@ def main():
     us = float(per.mean())
 
     if args.calib_copy_mb > 0:
-        src = torch.empty(args.calib_copy_mb * 2 ** 20, dtype=torch.uint8, device="cuda")
+        n = args.calib_copy_mb * 2 ** 20 // 4     # fp32 elements: reads and writes calib_copy_mb MiB
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
     gbps = abytes / us / 1e3
     tflops = flops / us / 1e6
+    traffic = read_traffic(cfg["name"])
     out = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -169,9 +259,9 @@ def main():
         "achieved_TFLOPs": round(tflops, 1),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": FP16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / FP16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None,
+                     "traffic": traffic,
                      "hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                             "frac": round(gbps / HBM_PEAK_GBPS, 4)}},
+                             "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": abytes}},
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -22,10 +22,21 @@
  *   C_i   M_i x N_i   fp16, row stride N_i elements (page 505431, the epilogue
  *                     of group_gemm_kernel_impl addresses C as row * N + col).
  *
- * Ownership: the caller allocates and owns every buffer.  The size arrays and
- * the pointer arrays are HOST memory, read only during the call; each element
- * pointer is a DEVICE pointer.  C_i is overwritten.  The library keeps no
- * state between calls apart from the thread-local error message.
+ * Ownership: the caller allocates and owns every operand and output.  The
+ * size arrays and the pointer arrays are HOST memory, read only during the
+ * call; each element pointer is a DEVICE pointer.  C_i is overwritten.
+ *
+ * Library state: tiles whose K range is split over several workgroups are
+ * summed through a device workspace (fp32 partial tiles and one counter per
+ * tile) that the library allocates with hipMalloc on the first call for a
+ * (device, stream) pair and keeps, growing it when a later call needs more
+ * (that call synchronises the stream first), until the process ends.  At
+ * most 2 x (compute units) x 128 KiB of partials plus 4 bytes per tile
+ * (16 KiB at least).  The counters return to zero at the end of every call,
+ * so calls on one stream may follow each other with no reset; calls on
+ * different streams use different workspaces.  A call that must allocate is
+ * not capturable into a HIP graph; once the workspace of a stream exists,
+ * calls of the same or smaller size on it allocate nothing.
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL is the default
  * stream) and the call returns without synchronising.
@@ -35,9 +46,10 @@
  *   NVFP4GG_INVALID_ARG  -1  g <= 0, a NULL array, a negative size, K_i not a
  *                            multiple of 16, a NULL or misaligned (16-byte)
  *                            device pointer of a non-empty operand
- *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle (an
- *                            operand above 2 GiB; see nvfp4_group_gemm)
- *   NVFP4GG_HIP_ERROR    -3  a HIP launch failed
+ *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle: a
+ *                            non-empty group with K_i % 256 != 0, an operand
+ *                            of 2 GiB or more, or M_i * N_i >= 2^31
+ *   NVFP4GG_HIP_ERROR    -3  a HIP call (launch, workspace allocation) failed
  * nvfp4_group_gemm_last_error() describes the last failure on this thread.
  */
 #ifndef NVFP4GG_H

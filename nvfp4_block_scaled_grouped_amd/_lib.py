@@ -92,6 +92,28 @@ def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0) -> int:
         arr(SFB, ctypes.c_void_p), arr(C, ctypes.c_void_p), ctypes.c_void_p(stream))
 
 
+class GroupGemmCall:
+    """A grouped GEMM call whose argument arrays are marshalled once.
+
+    Holds the ctypes copies of the sizes, the device addresses and the stream
+    handle, so that calling it repeats the same nvfp4_group_gemm call with no
+    per-call Python list work.  The addresses must stay valid while it is used.
+    """
+
+    def __init__(self, M, N, K, A, B, SFA, SFB, C, stream=0):
+        g = len(M)
+        lib = load()
+        arr = lambda vals, ct: (ct * g)(*vals)
+        self._fn = lib.nvfp4_group_gemm
+        self._args = (g, arr([int(v) for v in M], ctypes.c_int), arr([int(v) for v in N], ctypes.c_int),
+                      arr([int(v) for v in K], ctypes.c_int), arr(A, ctypes.c_void_p),
+                      arr(B, ctypes.c_void_p), arr(SFA, ctypes.c_void_p), arr(SFB, ctypes.c_void_p),
+                      arr(C, ctypes.c_void_p), ctypes.c_void_p(stream))
+
+    def __call__(self) -> int:
+        return self._fn(*self._args)
+
+
 def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None):
     """C_i = A_i . B_i^T for every group (see include/nvfp4gg.h).
 
