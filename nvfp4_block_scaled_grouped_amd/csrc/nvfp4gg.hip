@@ -54,6 +54,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <utility>
 
 #include "nvfp4gg.h"
@@ -70,16 +71,21 @@ typedef float f16x_t __attribute__((ext_vector_type(16)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 8;
+constexpr int kWaves = 8;                    // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
+constexpr int kNF = 2;                       // 32-column B fragments per wave
+constexpr int kColGroups = 4;                // 64-column groups of the tile
 constexpr int kKSteps = kStageK / 16;        // MFMA k-steps per stage (16 K each: 8 per lane half)
-constexpr int kFlushStages = 8;              // stages per partial accumulation (2048 K)
-constexpr int kSlotFloats = kWaves * kMaxFrags * kWave * 16;   // one partial tile
+constexpr int kHalfSteps = kKSteps / 2;      // k-steps of one wave per stage (its K half)
+constexpr int kMaxChainStages = 32;          // stages one fp32 chain accumulates (4096 K per wave)
+constexpr int kSlotFloats = kColGroups * kNF * kMaxFrags * kWave * 16;   // one partial tile
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
 constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
 
-static_assert(kTileN == kWaves * 32, "one 32-column fragment per wave");
+static_assert(kTileN == kColGroups * kNF * 32, "each column group owns kNF 32-column fragments");
+static_assert(kMaxFrags == 3, "the kernel instantiates m-blocks of 1, 2 and 3 fragments");
+static_assert(kWaves == 2 * kColGroups, "two K halves per column group");
 
 struct GroupArgs {
     const uint8_t* A;
@@ -129,14 +135,11 @@ __device__ __forceinline__ void scales4(uint32_t sc, _Float16* out)
     out[3] = s23.y;
 }
 
-__device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
+// Buffer loads at voffset (per lane) + soffset (wave-uniform, kept in an
+// SGPR so per-stage offsets cost no vector registers).
+__device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
 // LDS image of the dequantised A rows of one stage, in MFMA operand order:
@@ -144,6 +147,22 @@ __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off
 struct AStage {
     h8_t v[kMaxFrags][kKSteps][kWave];
 };
+
+// The workgroup's LDS: two A stages.  At the end of a segment the same
+// memory first carries the exchange of the two K halves' fp32 fragments
+// ([column group][B fragment][A fragment][quad][lane]) and then the fp16
+// output tile on its way to C (rows padded by 16 bytes against bank
+// conflicts).
+constexpr int kCTileStride = kTileN + 8;   // halves per LDS row of the output tile
+union SharedMem {
+    AStage a[2];
+    f4_t xch[kColGroups][kNF][kMaxFrags][4][kWave];
+    uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
+};
+static_assert(sizeof(f4_t) * kColGroups * kNF * kMaxFrags * 4 * kWave <= 2 * sizeof(AStage),
+              "the exchange fits in the A buffers");
+static_assert(sizeof(uint16_t) * kMaxFrags * kFragRows * kCTileStride <= 2 * sizeof(AStage),
+              "the output tile fits in the A buffers");
 
 // fp16 round-to-nearest-even (overflow to inf) of 4 floats, packed.
 __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d)
@@ -156,52 +175,129 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d)
     return w;
 }
 
-// Store the fp32 tile held in acc to C.  acc[fm] element r of lane (l32, h)
-// of wave w is C[m0 + 32 fm + l32][ncol + 8 (r / 4) + 4 h + r % 4], where
-// ncol is the wave's first column.
+// Workgroup barrier that hands LDS over between the waves: this wave's LDS
+// accesses complete before it, nobody's global loads are waited for (the
+// prefetched stages stay in flight), and the asm's memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int P>
+using Parity = std::integral_constant<int, P>;
+
+// The output tile of the workgroup, fp32 -> fp16 (round to nearest even,
+// overflow to inf), written to C through LDS so that every global store is
+// 16 contiguous bytes of a row.  Wave (cg, kh) holds fragment f = kh of
+// column group cg: own[fm] element r of lane (l32, h) is tile row
+// 32 fm + l32, tile column 64 cg + 32 kh + 8 (r / 4) + 4 h + r % 4.
+// Called by every thread of the workgroup; the LDS is free on return.
 template <int MF>
-__device__ __forceinline__ void store_c(const GroupArgs& ga, int m0, int ncol, const f16x_t* acc)
+__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0, const f16x_t* own,
+                                        int cg, int kh)
 {
     const int lane = threadIdx.x % kWave;
     const int l32 = lane & 31, h = lane >> 5;
-    const int M = ga.M, N = ga.N;
-    const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm) {
-        const int m = m0 + 32 * fm + l32;
-        if (m >= M) continue;
-        uint16_t* row = ga.C + (size_t)m * N;
+    for (int fm = 0; fm < MF; ++fm)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-            const int n = ncol + 8 * q4 + 4 * h;
-            if (n >= N) continue;
-            const f16x_t& v = acc[fm];
-            const uint2 w = pack4(v[4 * q4], v[4 * q4 + 1], v[4 * q4 + 2], v[4 * q4 + 3]);
-            if (vec_ok && n + 3 < N) {
-                *reinterpret_cast<uint2*>(row + n) = w;
-            } else {
-                const uint16_t o[4] = {(uint16_t)(w.x & 0xFFFF), (uint16_t)(w.x >> 16),
-                                       (uint16_t)(w.y & 0xFFFF), (uint16_t)(w.y >> 16)};
-                for (int e = 0; e < 4 && n + e < N; ++e) row[n + e] = o[e];
-            }
+            const int col = 64 * cg + 32 * kh + 8 * q4 + 4 * h;
+            *reinterpret_cast<uint2*>(&sm.ctile[32 * fm + l32][col]) =
+                pack4(own[fm][4 * q4], own[fm][4 * q4 + 1], own[fm][4 * q4 + 2], own[fm][4 * q4 + 3]);
+        }
+    lds_barrier();
+    const int M = ga.M, N = ga.N;
+    const int rows = M - m0 < MF * kFragRows ? M - m0 : MF * kFragRows;
+    const int chunk = threadIdx.x % (kTileN / 8);          // 8 columns = 16 bytes
+    const int n = n0 + 8 * chunk;
+    const bool vec_ok = (N & 7) == 0;
+    for (int r = threadIdx.x / (kTileN / 8); r < rows; r += kThreads / (kTileN / 8)) {
+        if (n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ctile[r][8 * chunk]);
+        uint16_t* dst = ga.C + (size_t)(m0 + r) * N + n;
+        if (vec_ok && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
         }
     }
+    lds_barrier();
 }
 
-// One segment [s_begin, s_end) of the stages of a tile with MF fragments.
+// One wave's fp32 fragment block of a partial tile (MF x 16 floats per
+// lane) at base, laid out in 1 KB lane-contiguous pieces.
 template <int MF>
-__device__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end, AStage* As,
-                            int* s_flag)
+__device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t base, const f16x_t* own)
+{
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(i4_t, f4_t{own[fm][4 * q], own[fm][4 * q + 1], own[fm][4 * q + 2],
+                                              own[fm][4 * q + 3]}),
+                r, base + (uint32_t)(fm * 4 + q) * (kWave * 16u), 0, kCoherent);
+}
+
+// acc (+)= the block stored by store_block at base (assign when first).
+template <int MF>
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t base, f16x_t* acc, bool first)
+{
+#pragma unroll
+    for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f4_t v = __builtin_bit_cast(
+                f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, base + (uint32_t)(fm * 4 + q) * (kWave * 16u), 0,
+                                                             kCoherent));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[fm][4 * q + e] = first ? v[e] : acc[fm][4 * q + e] + v[e];
+        }
+}
+
+// One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
+// workgroup's segment of a tile runs as chains of at most kMaxChainStages
+// stages (one chain for any K <= 8192); first_chain / last_chain place this
+// chain in its segment.
+//
+// Waves: wave w = 4 kh + cg owns columns [64 cg, 64 cg + 64) of the tile
+// (kNF = 2 fragments of 32) for all MF x 32 rows, over K half kh of every
+// stage (k-steps 8 kh .. 8 kh + 7).  The two K halves are independent fp32
+// chains, added through LDS at the end of the chain: splitting the sum into
+// two interleaved chains halves the magnitude each fp32 accumulator reaches
+// and the number of additions it makes, and capping a chain at 4096 K per
+// wave bounds both.  The chains of one segment meet in the workgroup's
+// scratch slot; the last one finishes the tile.
+//
+// Pipeline, per stage i of a chain:
+//   * B of stage i is in registers, loaded during stage i - 1: each 16-byte
+//     piece is re-loaded with stage i + 1 as soon as its four k-steps are
+//     dequantised.
+//   * A of stage i is in LDS buffer i % 2, dequantised during stage i - 1:
+//     wave w writes fragment w / 2, k-steps 8 (w % 2) .. 8 (w % 2) + 7, one
+//     k-step per k-step of its own MFMA loop, from raw bytes loaded during
+//     stage i - 2.
+//   * One LDS-only barrier ends the stage.
+template <int MF>
+__device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
+                                            bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
+    const int cg = wave % kColGroups;
+    const int kh = wave / kColGroups;
+    const int af = wave >> 1;            // A fragment this wave dequantises
+    const int ah = wave & 1;             // and which half of its k-steps
     const int lane = threadIdx.x % kWave;
     const int l32 = lane & 31;
     const int h = lane >> 5;
     const int M = ga.M, N = ga.N, K = ga.K;
     const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
-    const int ncol = pos.nb * kTileN + wave * 32;
+    const int ncol = pos.nb * kTileN + cg * (kNF * 32);
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 16;
 
@@ -210,130 +306,217 @@ __device__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin,
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
 
-    // B operand of lane (l32, h): row ncol + l32, bytes [64h, 64h+64) and
-    // scale bytes [8h, 8h+8) of each stage.
-    const uint32_t brow = (uint32_t)(ncol + l32);
-    const uint32_t offB = brow * row_bytes + 64u * h;
-    const uint32_t offSB = brow * row_scales + 8u * h;
-    // A loader: thread (r5, ah, af, ap) reads row m0 + 32 af + r5, bytes
-    // [64 ah + 32 ap, +32) and scale bytes [8 ah + 4 ap, +4) of each stage and
-    // writes k-steps 8 ap .. 8 ap + 7 of lane r5 + 32 ah of fragment af.
-    const int r5 = threadIdx.x & 31;
-    const int ah = (threadIdx.x >> 5) & 1;
-    const int af = (threadIdx.x >> 6) & 3;
-    const int ap = threadIdx.x >> 8;
-    const bool a_active = af < MF;
-    const uint32_t arow = (uint32_t)(m0 + 32 * af + r5);
-    const uint32_t offA = arow * row_bytes + 64u * ah + 32u * ap;
-    const uint32_t offSA = arow * row_scales + 8u * ah + 4u * ap;
-
-    auto store_a = [&](AStage& dst, const i4_t& c0, const i4_t& c1, uint32_t sc) {
-        _Float16 s[4];
-        scales4(sc, s);
+    // K order within a stage: lane half h owns K [128 h, 128 h + 128) and
+    // k-step j feeds dword j of it (8 codes, one scale block per 2 k-steps).
+    // B operand of lane (l32, h) in fragment f: row ncol + 32 f + l32, the 32
+    // bytes of k-steps 8 kh .. 8 kh + 7 of its half and their 4 scale bytes.
+    uint32_t offB[kNF], offSB[kNF];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) dst.v[af][8 * ap + t][r5 + 32 * ah] = dequant8((uint32_t)c0[t], s[t >> 1]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-            dst.v[af][8 * ap + 4 + t][r5 + 32 * ah] = dequant8((uint32_t)c1[t], s[2 + (t >> 1)]);
-    };
-
-    f16x_t acc[MF], part[MF];
-#pragma unroll
-    for (int f = 0; f < MF; ++f) {
-        acc[f] = f16x_t{};
-        part[f] = f16x_t{};
+    for (int f = 0; f < kNF; ++f) {
+        const uint32_t brow = (uint32_t)(ncol + 32 * f + l32);
+        offB[f] = brow * row_bytes + 64u * h + 32u * kh;
+        offSB[f] = brow * row_scales + 8u * h + 4u * kh;
     }
+    // A bytes this lane dequantises: row m0 + 32 af + l32, k-steps
+    // 8 ah .. 8 ah + 7 of lane half h.
+    const bool a_active = af < MF;
+    const uint32_t arow = (uint32_t)(m0 + 32 * af + l32);
+    const uint32_t offA = arow * row_bytes + 64u * h + 32u * ah;
+    const uint32_t offSA = arow * row_scales + 8u * h + 4u * ah;
 
-    // Prologue: stage s_begin of A into LDS buffer 0 and of B into registers.
-    const uint32_t sb0 = (uint32_t)s_begin * (kStageK / 2);
-    const uint32_t ss0 = (uint32_t)s_begin * (kStageK / 16);
-    if (a_active) store_a(As[0], load16(rA, offA + sb0), load16(rA, offA + sb0 + 16), load4(rSA, offSA + ss0));
-    i4_t b[4];
+    f16x_t part[kNF][kMaxFrags];
+    f16x_t own[kMaxFrags];   // after a chain: fragment f = kh of this wave's column group, both K halves
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
+    // This wave's block of a slot: [column group][B fragment] blocks of
+    // kMaxFrags x 4 x 1 KB; wave (cg, kh) owns block (cg, kh).
+    const uint32_t wave_in_slot =
+        (uint32_t)(cg * kNF + kh) * (kMaxFrags * 4) * (kWave * 16u) + (uint32_t)lane * 16u;
+    const uint32_t scratch_base =
+        (uint32_t)scratch_slot(blockIdx.x) * kSlotFloats * 4u + wave_in_slot;
+
+    {
+        const int c_begin = s_begin;
+        const int n = s_end - s_begin;
+
+        // Register stage buffers, each one stage ahead of its use: B of the
+        // stage being multiplied (each 16-byte piece re-loaded with the next
+        // stage's as soon as its four k-steps are dequantised), and the raw A
+        // of the stage being dequantised into LDS (likewise re-loaded with
+        // the stage after).
+        i4_t bq[kNF][2];
+        uint32_t bs[kNF];
+        i4_t aq[2] = {i4_t{}, i4_t{}};
+        uint32_t as = 0u;
+
+        // Prologue: B of stage 0 and A of stages 0 and 1 in flight; stage 0
+        // of A into LDS buffer 0.
+        {
+            const uint32_t sbyte = (uint32_t)c_begin * (kStageK / 2);
+            const uint32_t sscale = (uint32_t)c_begin * (kStageK / 16);
+            i4_t a0[2] = {i4_t{}, i4_t{}};
+            uint32_t as0 = 0u;
+            if (a_active) {
+                a0[0] = load16(rA, offA, sbyte);
+                a0[1] = load16(rA, offA + 16, sbyte);
+                as0 = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale, 0);
+            }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) b[c] = load16(rB, offB + sb0 + 16 * c);
-    uint32_t bsc0 = load4(rSB, offSB + ss0), bsc1 = load4(rSB, offSB + ss0 + 4);
-    __syncthreads();
-
-    const int n = s_end - s_begin;
-    for (int i = 0; i < n; ++i) {
-        const int buf = i & 1;
-        const bool more = i + 1 < n;
-        const uint32_t nbytes = (uint32_t)(s_begin + i + 1) * (kStageK / 2);
-        const uint32_t nscales = (uint32_t)(s_begin + i + 1) * (kStageK / 16);
-        // A of the next stage (dequantised into the other buffer at the end).
-        i4_t na0 = i4_t{}, na1 = i4_t{};
-        uint32_t nasc = 0;
-        if (a_active && more) {
-            na0 = load16(rA, offA + nbytes);
-            na1 = load16(rA, offA + nbytes + 16);
-            nasc = load4(rSA, offSA + nscales);
+            for (int f = 0; f < kNF; ++f) {
+                bq[f][0] = load16(rB, offB[f], sbyte);
+                bq[f][1] = load16(rB, offB[f] + 16, sbyte);
+                bs[f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale, 0);
+            }
+            if (a_active && n > 1) {
+                aq[0] = load16(rA, offA, sbyte + kStageK / 2);
+                aq[1] = load16(rA, offA + 16, sbyte + kStageK / 2);
+                as = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale + kStageK / 16, 0);
+            }
+            if (a_active) {
+                _Float16 sa[4];
+                scales4(as0, sa);
+#pragma unroll
+                for (int u = 0; u < kHalfSteps; ++u)
+                    sm.a[0].v[af][kHalfSteps * ah + u][lane] = dequant8((uint32_t)a0[u >> 2][u & 3], sa[u >> 1]);
+            }
         }
-        _Float16 sb[8];
-        scales4(bsc0, sb);
-        scales4(bsc1, sb + 4);
-        if (more) {
-            bsc0 = load4(rSB, offSB + nscales);
-            bsc1 = load4(rSB, offSB + nscales + 4);
-        }
+#pragma unroll
+        for (int f = 0; f < kNF; ++f)
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm) part[f][fm] = f16x_t{};
+        lds_barrier();
 
+        auto stage = [&](auto parity, int i) {
+            constexpr int p = decltype(parity)::value;
+            const bool has1 = i + 1 < n;
+            const bool has2 = i + 2 < n;
+            const uint32_t sbyte1 = (uint32_t)(c_begin + i + 1) * (kStageK / 2);
+            const uint32_t sscale1 = (uint32_t)(c_begin + i + 1) * (kStageK / 16);
+            const uint32_t sbyte2 = sbyte1 + kStageK / 2;
+            const uint32_t sscale2 = sscale1 + kStageK / 16;
+
+            _Float16 sbf[kNF][4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+            for (int f = 0; f < kNF; ++f) scales4(bs[f], sbf[f]);
+            _Float16 sa[4];
+            scales4(as, sa);
+            if (has1) {
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = 4 * c + jj;
-                const h8_t bv = dequant8((uint32_t)b[c][jj], sb[j >> 1]);
+                for (int f = 0; f < kNF; ++f) bs[f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale1, 0);
+            }
+            if (a_active && has2) as = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale2, 0);
+            const bool a_store = a_active && has1;
+
+            // k-steps: each A fragment is re-read from LDS for k-step u + 1
+            // as soon as its two MFMAs of k-step u are issued (the B dequant
+            // latency is covered by the other wave of the SIMD).  The
+            // scheduling barrier at the end of each k-step keeps the compiler
+            // from hoisting work across k-steps (register pressure).
+            h8_t av[MF];
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm) av[fm] = sm.a[p].v[fm][kHalfSteps * kh][lane];
+#pragma unroll
+            for (int u = 0; u < kHalfSteps; ++u) {
+                h8_t bv[kNF];
+#pragma unroll
+                for (int f = 0; f < kNF; ++f) bv[f] = dequant8((uint32_t)bq[f][u >> 2][u & 3], sbf[f][u >> 1]);
+                if (a_store)
+                    sm.a[p ^ 1].v[af][kHalfSteps * ah + u][lane] =
+                        dequant8((uint32_t)aq[u >> 2][u & 3], sa[u >> 1]);
 #pragma unroll
                 for (int fm = 0; fm < MF; ++fm) {
-                    const h8_t av = As[buf].v[fm][j][lane];
-                    part[fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv, av, part[fm], 0, 0, 0);
-                }
-            }
-            // This 16-byte piece of B is consumed: fetch the next stage's.
-            if (more) b[c] = load16(rB, offB + nbytes + 16 * c);
-        }
-
-        if (((i + 1) % kFlushStages) == 0 || !more) {
 #pragma unroll
-            for (int f = 0; f < MF; ++f) {
-                acc[f] += part[f];
-                part[f] = f16x_t{};
+                    for (int f = 0; f < kNF; ++f)
+                        part[f][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[f], av[fm], part[f][fm], 0, 0, 0);
+                    if (u + 1 < kHalfSteps) av[fm] = sm.a[p].v[fm][kHalfSteps * kh + u + 1][lane];
+                }
+                // Piece c (k-steps 4c .. 4c+3) of B and of the raw A is now
+                // dequantised in full: fetch the next stage's.
+                if ((u & 3) == 3 && has1) {
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) bq[f][u >> 2] = load16(rB, offB[f] + 16 * (u >> 2), sbyte1);
+                }
+                if ((u & 3) == 3 && a_active && has2) aq[u >> 2] = load16(rA, offA + 16 * (u >> 2), sbyte2);
+                __builtin_amdgcn_sched_barrier(0);
             }
+            lds_barrier();
+        };
+
+        for (int i = 0; i < n; i += 2) {
+            stage(Parity<0>{}, i);
+            if (i + 1 >= n) break;
+            stage(Parity<1>{}, i + 1);
         }
 
-        if (a_active && more) store_a(As[buf ^ 1], na0, na1, nasc);
-        __syncthreads();
+        // Add the two K halves through LDS (the A buffers are free: every
+        // wave is past the last stage's barrier).  Wave (cg, kh) hands
+        // fragment 1 - kh to its partner (cg, 1 - kh) and keeps fragment kh,
+        // so both halves of the workgroup carry the epilogue.  The indices
+        // are spelled out per kh to keep the register arrays statically
+        // indexed.
+        if (kh == 0) {
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sm.xch[cg][1][fm][q][lane] = f4_t{part[1][fm][4 * q], part[1][fm][4 * q + 1],
+                                                      part[1][fm][4 * q + 2], part[1][fm][4 * q + 3]};
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    sm.xch[cg][0][fm][q][lane] = f4_t{part[0][fm][4 * q], part[0][fm][4 * q + 1],
+                                                      part[0][fm][4 * q + 2], part[0][fm][4 * q + 3]};
+        }
+        lds_barrier();
+        if (kh == 0) {
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm) own[fm] = part[0][fm];
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < MF; ++fm) own[fm] = part[1][fm];
+        }
+#pragma unroll
+        for (int fm = 0; fm < MF; ++fm)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f4_t v = sm.xch[cg][kh][fm][q][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) own[fm][4 * q + e] += v[e];
+            }
+        lds_barrier();   // the exchange is read before anything else is written to the LDS
+    }
+    // Chains of one segment meet in the scratch slot.
+    if (!first_chain) load_block<MF>(rP, scratch_base, own, false);
+    if (!last_chain) {
+        store_block<MF>(rP, scratch_base, own);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        return;
     }
 
-    // Finish the tile: alone, or as one of several contributors.
-    const int unit = pos.frags + 1;
+    // Finish the tile: alone, or as one of several contributors.  Every
+    // wave holds its fragment of the segment's sum in own.
+    const int unit = unit_cost(pos.frags);
     const int64_t c_first = pos.tile_cost0;
     const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
     const int w_first = owner(args.W, args.G, c_first);
     const int w_last = owner(args.W, args.G, c_last);
+    const int n0 = pos.nb * kTileN;
     if (w_first == w_last) {
-        store_c<MF>(ga, m0, ncol, acc);
+        store_c<MF>(sm, ga, m0, n0, own, cg, kh);
         return;
     }
     const int me = blockIdx.x;
     const int tile = tile_index(args.sched, pos);
-    // Partial tile -> this workgroup's slot.  The stores carry the
-    // device-scope coherence bit (sc1), so they are written through past
+    // Partial tile -> this workgroup's slot (partial_slot).  The stores carry
+    // the device-scope coherence bit (sc1), so they are written through past
     // this XCD's L2; waiting for them before the counter update publishes
     // them to whichever workgroup finishes the tile, with no cache flush.
-    const __amdgpu_buffer_rsrc_t rP = make_rsrc(args.partials, (uint32_t)(2 * args.G) * kSlotFloats * 4u);
-    {
-        const uint32_t slot_off = (uint32_t)(me * 2 + (me < w_last ? 1 : 0)) * kSlotFloats * 4u;
-#pragma unroll
-        for (int fm = 0; fm < MF; ++fm) {
-            const uint32_t off = slot_off + (uint32_t)((wave * kMaxFrags + fm) * kWave + lane) * 64u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(i4_t, f4_t{acc[fm][4 * q], acc[fm][4 * q + 1], acc[fm][4 * q + 2],
-                                                  acc[fm][4 * q + 3]}),
-                    rP, off + 16u * q, 0, kCoherent);
-        }
-    }
+    auto slot_base = [&](int w) {
+        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + wave_in_slot;
+    };
+    store_block<MF>(rP, slot_base(me), own);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -345,40 +528,21 @@ __device__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin,
     const bool last = *s_flag != 0;
     __syncthreads();   // s_flag is reused by the next segment
     if (!last) return;
-    // Sum every contributor's partial (this workgroup's included) in
-    // workgroup order, so the result does not depend on who arrived last.
-    // The loads carry the device-scope coherence bit as well.
-    for (int w = w_first; w <= w_last; ++w) {
-        const uint32_t slot_off = (uint32_t)(w * 2 + (w < w_last ? 1 : 0)) * kSlotFloats * 4u;
-#pragma unroll
-        for (int fm = 0; fm < MF; ++fm) {
-            const uint32_t off = slot_off + (uint32_t)((wave * kMaxFrags + fm) * kWave + lane) * 64u;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4_t v = __builtin_bit_cast(
-                    f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, off + 16u * q, 0, kCoherent));
-                if (w == w_first) {
-                    acc[fm][4 * q] = v.x;
-                    acc[fm][4 * q + 1] = v.y;
-                    acc[fm][4 * q + 2] = v.z;
-                    acc[fm][4 * q + 3] = v.w;
-                } else {
-                    acc[fm][4 * q] += v.x;
-                    acc[fm][4 * q + 1] += v.y;
-                    acc[fm][4 * q + 2] += v.z;
-                    acc[fm][4 * q + 3] += v.w;
-                }
-            }
-        }
-    }
-    store_c<MF>(ga, m0, ncol, acc);
+    // Sum the contributors' partials in workgroup order, so the result does
+    // not depend on who arrived last.  When this workgroup is the first
+    // contributor its partial is still in registers; otherwise it is read
+    // back like the others.  The loads carry the device-scope coherence bit
+    // as well.
+    for (int w = me == w_first ? w_first + 1 : w_first; w <= w_last; ++w)
+        load_block<MF>(rP, slot_base(w), own, w == w_first);
+    store_c<MF>(sm, ga, m0, n0, own, cg, kh);
     if (threadIdx.x == 0)
         __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ AStage As[2];
+    __shared__ SharedMem sm;
     __shared__ int s_flag;
 
     const int w = blockIdx.x;
@@ -386,15 +550,19 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
     Pos pos = locate(args.sched, args.ngroups, boundary(args.W, args.G, w));
     while (pos.group < args.ngroups && stage_cost(pos, pos.stage) < b1) {
         const GroupSched& gs = args.sched[pos.group];
-        const int unit = pos.frags + 1;
+        const int unit = unit_cost(pos.frags);
         // Stages of this tile that start before b1.
         const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
         const int s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
-        switch (pos.frags) {
-            case 1: run_segment<1>(args, pos, pos.stage, s_end, As, &s_flag); break;
-            case 2: run_segment<2>(args, pos, pos.stage, s_end, As, &s_flag); break;
-            case 3: run_segment<3>(args, pos, pos.stage, s_end, As, &s_flag); break;
-            default: run_segment<4>(args, pos, pos.stage, s_end, As, &s_flag); break;
+        // The segment runs as chains of at most kMaxChainStages stages.
+        for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
+            const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
+            const bool first = c0 == pos.stage, last = c1 == s_end;
+            switch (pos.frags) {
+                case 1: run_segment<1>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                case 2: run_segment<2>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                default: run_segment<3>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+            }
         }
         if (s_end < gs.stages) break;
         pos = locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages);
@@ -452,12 +620,12 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Minimum cost handed to one workgroup: keeps every workgroup range longer
-// than the costliest stage (kMaxFrags + 1 units), which the fixup relies on.
-constexpr int64_t kMinUnitsPerWG = 16;
-static_assert(kMinUnitsPerWG >= kMaxFrags + 1, "a workgroup range must hold a stage");
+// than the costliest stage, which the fixup relies on.
+constexpr int64_t kMinUnitsPerWG = 8;
+static_assert(kMinUnitsPerWG >= kMaxFrags + kStageFixedCost, "a workgroup range must hold a stage");
 
-// Workspace of the split-tile fixup, one per (device, stream): the partial
-// tiles and the per-tile counters (zero between calls; the last contributor
+// Workspace of the split-tile fixup, one per (device, stream): three
+// partial-tile slots per workgroup and the per-tile counters (zero between calls; the last contributor
 // of a tile resets its counter).  Allocated on first use and kept.
 struct Workspace {
     float* partials = nullptr;
@@ -473,7 +641,7 @@ int get_workspace(int dev, hipStream_t s, int G, int tiles, Workspace& out)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& w = g_ws[std::make_pair(dev, (void*)s)];
-    const size_t need_slots = 2 * (size_t)G;
+    const size_t need_slots = kSlotsPerWG * (size_t)G;
     if (w.slots < need_slots) {
         if (w.partials) {
             if (hipStreamSynchronize(s) != hipSuccess || hipFree(w.partials) != hipSuccess)

@@ -15,8 +15,9 @@
 //     n-block, then m-block, so the m-blocks that share a B strip are
 //     adjacent in the order.
 //   * stage: kStageK consecutive K of a tile.  A stage of a tile with f
-//     fragments costs f + 1 units (MFMA work grows with f; the B work of
-//     the stage does not).
+//     fragments costs f + kStageFixedCost units: the MFMA work grows with f,
+//     while the B stream and its dequantisation do not (measured on MI355X:
+//     a stage takes about 1.5 + 0.5 f microseconds).
 //   * Workgroup w of G takes the cost range [w*W/G, (w+1)*W/G), rounded up
 //     to stage starts, so every stage belongs to exactly one workgroup.
 #ifndef NVFP4GG_SCHEDULE_H
@@ -32,11 +33,12 @@
 
 namespace nvfp4sched {
 
-constexpr int kMaxFrags = 4;       // fragments per m-block
+constexpr int kMaxFrags = 3;       // fragments per m-block
 constexpr int kFragRows = 32;      // rows per fragment
 constexpr int kTileN = 256;        // columns per n-block
 constexpr int kStageK = 256;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
+constexpr int kStageFixedCost = 3; // cost units of a stage that do not scale with its fragments
 
 struct GroupSched {
     int64_t cost_begin;   // cost units before this group
@@ -48,6 +50,9 @@ struct GroupSched {
 };
 
 NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
+
+// Cost of one stage of a tile with f fragments.
+NVFP4_HD int unit_cost(int f) { return f + kStageFixedCost; }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
 NVFP4_HD int mblock_frags(int F, int nmb, int i)
@@ -66,7 +71,7 @@ NVFP4_HD int mblock_first_frag(int F, int nmb, int i)
 // Cost of one n-block column of a group (all m-blocks, all stages).
 NVFP4_HD int64_t column_cost(const GroupSched& g)
 {
-    return (int64_t)(g.frags + g.mblocks) * g.stages;
+    return (int64_t)(g.frags + kStageFixedCost * g.mblocks) * g.stages;
 }
 
 NVFP4_HD int64_t group_cost(const GroupSched& g) { return column_cost(g) * g.nblocks; }
@@ -99,16 +104,18 @@ NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
         r.group = gi;
         r.nb = (int)(q / cc);
         q -= (int64_t)r.nb * cc;
-        // Cost before m-block i of a column is (first_frag(i) + i) * stages.
+        // Cost before m-block i of a column is
+        // (first_frag(i) + kStageFixedCost * i) * stages.
         int mb = 0;
         while (mb + 1 < g.mblocks &&
-               (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb + 1) + mb + 1) * g.stages <= q)
+               (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb + 1) + kStageFixedCost * (mb + 1)) * g.stages <= q)
             ++mb;
         r.mb = mb;
         r.frags = mblock_frags(g.frags, g.mblocks, mb);
-        const int64_t mcost0 = (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb) + mb) * g.stages;
+        const int64_t mcost0 =
+            (int64_t)(mblock_first_frag(g.frags, g.mblocks, mb) + kStageFixedCost * mb) * g.stages;
         q -= mcost0;
-        const int unit = r.frags + 1;
+        const int unit = unit_cost(r.frags);
         r.stage = (int)((q + unit - 1) / unit);
         r.tile_cost0 = g.cost_begin + (int64_t)r.nb * cc + mcost0;
         if (r.stage < g.stages) return r;
@@ -117,7 +124,7 @@ NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
 }
 
 // Cost position of stage s of the tile at position p.
-NVFP4_HD int64_t stage_cost(const Pos& p, int s) { return p.tile_cost0 + (int64_t)s * (p.frags + 1); }
+NVFP4_HD int64_t stage_cost(const Pos& p, int s) { return p.tile_cost0 + (int64_t)s * unit_cost(p.frags); }
 
 // Workgroup boundary b_w = floor(w * W / G) (w = 0..G).
 NVFP4_HD int64_t boundary(int64_t W, int G, int w) { return (W * (int64_t)w) / G; }
@@ -132,6 +139,15 @@ NVFP4_HD int owner(int64_t W, int G, int64_t c)
     while (w + 1 < G && boundary(W, G, (int)w + 1) <= c) ++w;
     return (int)w;
 }
+
+// Workspace slots of workgroup w (one fp32 partial tile each): a tile split
+// over workgroups w_first..w_last gets one partial from each contributor; w
+// writes it to slot 0 when it is the tile's last contributor (the tile is the
+// first of w's range) and to slot 1 otherwise (the tile is the last of w's
+// range; a range inside one tile also uses slot 1).  Slot 2 is w's scratch.
+constexpr int kSlotsPerWG = 3;
+NVFP4_HD int partial_slot(int w, int w_last) { return w * kSlotsPerWG + (w < w_last ? 1 : 0); }
+NVFP4_HD int scratch_slot(int w) { return w * kSlotsPerWG + 2; }
 
 // Global tile index of a position.
 NVFP4_HD int tile_index(const GroupSched* gs, const Pos& p)

@@ -57,7 +57,7 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
         while (pos.group < ng && stage_cost(pos, pos.stage) < b1) {
             CHECK(++guard < 1000000, "runaway walk");
             const GroupSched& g = gs[pos.group];
-            const int unit = pos.frags + 1;
+            const int unit = unit_cost(pos.frags);
             const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
             const int s_end = s_end64 < g.stages ? (int)s_end64 : g.stages;
             CHECK(s_end > pos.stage, "empty segment w=%d", w);
@@ -75,11 +75,13 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
             const int wf = owner(W, G, c_first), wl = owner(W, G, c_last);
             CHECK(wf <= w && w <= wl, "contributor range");
             if (wf != wl) {
-                const int slot = w < wl ? 1 : 0;
+                const int slot = partial_slot(w, wl);
                 auto sk = std::make_pair(w, slot);
                 CHECK(!slot_use.count(sk), "slot reused w=%d slot=%d", w, slot);
                 slot_use[sk] = t;
-                CHECK(w * 2 + slot < 2 * G, "slot bound");
+                CHECK(slot >= w * kSlotsPerWG && slot < (w + 1) * kSlotsPerWG, "slot outside w's slots");
+                CHECK(slot != scratch_slot(w), "partial in the scratch slot");
+                CHECK(slot < kSlotsPerWG * G, "slot bound");
             }
             if (s_end < g.stages) break;
             pos = locate(gs, ng, pos.tile_cost0 + (int64_t)unit * g.stages);
@@ -100,11 +102,11 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
 int main()
 {
     // The five workloads.
-    run_case({64, 96}, {256, 256}, {512, 512}, 256, 16);
-    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256, 16);
-    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256, 16);
-    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256, 16);
-    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256, 16);
+    run_case({64, 96}, {256, 256}, {512, 512}, 256, 8);
+    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256, 8);
+    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256, 8);
+    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256, 8);
+    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256, 8);
     // Random shapes and grid sizes.
     std::mt19937 rng(12345);
     for (int it = 0; it < 3000; ++it) {
@@ -115,7 +117,7 @@ int main()
             N.push_back(1 + rng() % 3000);
             K.push_back(256 * (1 + rng() % 12));
         }
-        run_case(M, N, K, 1 + rng() % 300, 5 + rng() % 40);
+        run_case(M, N, K, 1 + rng() % 300, kMaxFrags + kStageFixedCost + rng() % 40);
         if (fails) break;
     }
     if (fails) { std::printf("FAILED %d\n", fails); return 1; }

@@ -196,3 +196,22 @@ def test_workload_sampled(nv, oracle_lib, cfg):
         worst = max(worst, _compare.assert_close(np.array(y), np.array(r), np.array(x),
                                                  "%s group %d" % (cfg["name"], i)))
     _say("  worst |err|/tol on samples: %.3f" % worst)
+
+
+def test_long_segments_run_as_several_chains(nv, oracle_lib):
+    """K = 17408 (68 stages) over 128 column blocks: every workgroup's range
+    covers more than 32 stages of a tile, so its segment runs as two chains
+    that meet in the scratch slot.  Checked on sampled elements."""
+    M, N, K = [96], [32768], [17408]
+    _say("long segments M=%s N=%s K=%s" % (M, N, K))
+    A, B, SA, SB = workloads.make_inputs(M, N, K, 31)
+    C = _run_gpu(nv, M, N, K, A, B, SA, SB)[0]
+    assert not np.isnan(C.astype(np.float32)).any()
+    rng = np.random.default_rng(7)
+    y, r, x = [], [], []
+    for m, n in _sample_points(M[0], N[0], rng, 300):
+        c16, ex = oracle_lib.gemm_element(M[0], N[0], K[0], A[0], B[0], SA[0], SB[0], m, n)
+        y.append(C[m, n])
+        r.append(np.uint16(c16).view(np.float16))
+        x.append(ex)
+    _compare.assert_close(np.array(y), np.array(r), np.array(x), "long segments")
