@@ -31,7 +31,7 @@
  * tile) that the library allocates with hipMalloc on the first call for a
  * (device, stream) pair and keeps, growing it when a later call needs more
  * (that call synchronises the stream first), until the process ends.  At
- * most 2 x (compute units) x 128 KiB of partials plus 4 bytes per tile
+ * most 3 x (compute units) x 96 KiB of partials plus 4 bytes per tile
  * (16 KiB at least).  The counters return to zero at the end of every call,
  * so calls on one stream may follow each other with no reset; calls on
  * different streams use different workspaces.  A call that must allocate is

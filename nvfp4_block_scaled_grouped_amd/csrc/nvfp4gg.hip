@@ -19,23 +19,22 @@
 //     (its scale operand contributes only a power of two, so it is passed
 //     1.0), then v_pk_mul_f16 multiplies by the E4M3 scale converted to fp16
 //     (exact: every E4M3 value is an fp16 value).
-//   * Tile: one workgroup of 8 waves per CU owns up to 128 rows of A_i
-//     (1..4 fragments of 32 rows) x 256 columns of B_i; wave w owns columns
-//     [32w, 32w+32) of the tile for all its rows.  A is shared: each 256-K
-//     stage of the tile's A rows is dequantised once by the workgroup into
-//     LDS as fp16, already in MFMA operand order, and every wave reads it with
-//     16-byte LDS loads.  B is private to a wave: each lane loads its own MFMA
-//     operand bytes (a full 128-byte line per row per stage) straight into
-//     registers and dequantises them there, so one dequantised B fragment
-//     feeds up to 4 MFMAs.
-//   * K order: the sum over K is order-free.  Within a 256-K stage, lane half
-//     h (lanes 32h..32h+31) owns K [128h, 128h+128) and feeds, in MFMA k-step
-//     j, the 8 codes of dword j of that range.  A and B use the same
-//     assignment, so every pair (a_k, b_k) meets in the same MFMA slot.
-//   * Accumulation is hierarchical: each stretch of at most 2048 K
-//     accumulates into a fresh fp32 tile that is then added into the running
-//     tile, which keeps the rounding error of long K sums small next to
-//     outputs near zero.
+//   * Tile: one workgroup of 8 waves per CU owns up to 96 rows of A_i
+//     (1..3 fragments of 32 rows) x 256 columns of B_i.  Wave w = 4 kh + cg
+//     owns columns [64 cg, 64 cg + 64) for all rows, over K half kh of every
+//     256-K stage.  A is shared: each stage of the tile's A rows is
+//     dequantised once by the workgroup into LDS as fp16, already in MFMA
+//     operand order, and the waves read it with 16-byte LDS loads.  B is
+//     private to a wave: each lane loads its own MFMA operand bytes straight
+//     into registers and dequantises them there, so one dequantised B
+//     fragment feeds up to 3 MFMAs.
+//   * K order: the sum over K is order-free.  A and B use the same order, so
+//     every pair (a_k, b_k) meets in the same MFMA slot; it is chosen so that
+//     the two lanes holding a row read one contiguous 64-byte run.
+//   * Accumulation: the two K halves of a stage are summed by different
+//     waves into separate fp32 accumulators (two interleaved chains, each at
+//     most 4096 K long), added at the end; this keeps the rounding error of
+//     long K sums small next to outputs near zero.
 //   * Schedule: the work is the list of (tile, stage) units (schedule.h); a
 //     persistent grid of one workgroup per CU takes equal-cost contiguous
 //     ranges of it, so ragged groups fill the chip in one launch.  A tile
@@ -82,6 +81,12 @@ constexpr int kSlotFloats = kColGroups * kNF * kMaxFrags * kWave * 16;   // one 
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
 constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
+
+// Issue-order hints that interleave the B dequantisation with the MFMAs of
+// each k-step (0 leaves the order to the compiler).
+#ifndef NVFP4_INTERLEAVE
+#define NVFP4_INTERLEAVE 1
+#endif
 
 static_assert(kTileN == kColGroups * kNF * 32, "each column group owns kNF 32-column fragments");
 static_assert(kMaxFrags == 3, "the kernel instantiates m-blocks of 1, 2 and 3 fragments");
@@ -142,6 +147,7 @@ __device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
     return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+
 // LDS image of the dequantised A rows of one stage, in MFMA operand order:
 // [fragment][k-step][lane] x 8 fp16 (64 KB).
 struct AStage {
@@ -154,10 +160,15 @@ struct AStage {
 // output tile on its way to C (rows padded by 16 bytes against bank
 // conflicts).
 constexpr int kCTileStride = kTileN + 8;   // halves per LDS row of the output tile
-union SharedMem {
-    AStage a[2];
-    f4_t xch[kColGroups][kNF][kMaxFrags][4][kWave];
-    uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
+struct SharedMem {
+    union {
+        AStage a[2];
+        f4_t xch[kColGroups][kNF][kMaxFrags][4][kWave];
+        uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
+    };
+    // Target of the A-store of waves that have no A fragment in the tile
+    // (their writes are discarded), so the k-step needs no branch.
+    h8_t discard[kKSteps / 2][kWave];
 };
 static_assert(sizeof(f4_t) * kColGroups * kNF * kMaxFrags * 4 * kWave <= 2 * sizeof(AStage),
               "the exchange fits in the A buffers");
@@ -306,23 +317,29 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
 
-    // K order within a stage: lane half h owns K [128 h, 128 h + 128) and
-    // k-step j feeds dword j of it (8 codes, one scale block per 2 k-steps).
+    // K order within a stage (the sum is order-free; A and B use the same
+    // order): k-step j = 8 q + u (K half q, u < 8) feeds lane half h the 8
+    // codes at K 128 q + 64 h + 8 u, i.e. dword u of the 32 bytes
+    // [64 q + 32 h, +32) of the row's stage bytes, whose scale block is
+    // 8 q + 4 h + u / 2.  So the two lanes of a row read one contiguous,
+    // 64-byte aligned run per K half.
     // B operand of lane (l32, h) in fragment f: row ncol + 32 f + l32, the 32
-    // bytes of k-steps 8 kh .. 8 kh + 7 of its half and their 4 scale bytes.
+    // bytes of its half of K half kh and their 4 scale bytes.
     uint32_t offB[kNF], offSB[kNF];
 #pragma unroll
     for (int f = 0; f < kNF; ++f) {
         const uint32_t brow = (uint32_t)(ncol + 32 * f + l32);
-        offB[f] = brow * row_bytes + 64u * h + 32u * kh;
-        offSB[f] = brow * row_scales + 8u * h + 4u * kh;
+        offB[f] = brow * row_bytes + 64u * kh + 32u * h;
+        offSB[f] = brow * row_scales + 8u * kh + 4u * h;
     }
-    // A bytes this lane dequantises: row m0 + 32 af + l32, k-steps
-    // 8 ah .. 8 ah + 7 of lane half h.
+    // A bytes this lane dequantises: row m0 + 32 af + l32, its half of K half
+    // ah (k-steps 8 ah .. 8 ah + 7).
     const bool a_active = af < MF;
-    const uint32_t arow = (uint32_t)(m0 + 32 * af + l32);
-    const uint32_t offA = arow * row_bytes + 64u * h + 32u * ah;
-    const uint32_t offSA = arow * row_scales + 8u * h + 4u * ah;
+    // Waves without a fragment of this tile load (and discard) the rows of
+    // fragment af % MF, which the L1 already fetches for its owner.
+    const uint32_t arow = (uint32_t)(m0 + 32 * (af % MF) + l32);
+    const uint32_t offA = arow * row_bytes + 64u * ah + 32u * h;
+    const uint32_t offSA = arow * row_scales + 8u * ah + 4u * h;
 
     f16x_t part[kNF][kMaxFrags];
     f16x_t own[kMaxFrags];   // after a chain: fragment f = kh of this wave's column group, both K halves
@@ -352,8 +369,8 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         // Prologue: B of stage 0 and A of stages 0 and 1 in flight; stage 0
         // of A into LDS buffer 0.
         {
-            const uint32_t sbyte = (uint32_t)c_begin * (kStageK / 2);
-            const uint32_t sscale = (uint32_t)c_begin * (kStageK / 16);
+            const uint32_t sbyte = __builtin_amdgcn_readfirstlane(c_begin * (kStageK / 2));
+            const uint32_t sscale = __builtin_amdgcn_readfirstlane(c_begin * (kStageK / 16));
             i4_t a0[2] = {i4_t{}, i4_t{}};
             uint32_t as0 = 0u;
             if (a_active) {
@@ -390,10 +407,15 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             constexpr int p = decltype(parity)::value;
             const bool has1 = i + 1 < n;
             const bool has2 = i + 2 < n;
-            const uint32_t sbyte1 = (uint32_t)(c_begin + i + 1) * (kStageK / 2);
-            const uint32_t sscale1 = (uint32_t)(c_begin + i + 1) * (kStageK / 16);
+            // Stage offsets are wave-uniform; readfirstlane keeps them in
+            // SGPRs (the buffer loads' soffset) where the compiler would
+            // otherwise not prove it.
+            const uint32_t sbyte1 = __builtin_amdgcn_readfirstlane((c_begin + i + 1) * (kStageK / 2));
+            const uint32_t sscale1 = __builtin_amdgcn_readfirstlane((c_begin + i + 1) * (kStageK / 16));
             const uint32_t sbyte2 = sbyte1 + kStageK / 2;
             const uint32_t sscale2 = sscale1 + kStageK / 16;
+            const uint32_t sbyte_n = has1 ? sbyte1 : sbyte1 - kStageK / 2;    // B loads: next stage, or this one
+            const uint32_t sbyte_nn = has2 ? sbyte2 : sbyte1 - kStageK / 2;   // A loads: stage i + 2, or this one
 
             _Float16 sbf[kNF][4];
 #pragma unroll
@@ -405,38 +427,71 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
                 for (int f = 0; f < kNF; ++f) bs[f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale1, 0);
             }
             if (a_active && has2) as = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale2, 0);
-            const bool a_store = a_active && has1;
+            // Where this wave's A dequantisation goes: its fragment of the
+            // next stage's buffer, or the discard area.  (In a chain's last
+            // stage the next buffer is written but never read.)
+            h8_t* const a_dst = a_active ? &sm.a[p ^ 1].v[af][kHalfSteps * ah][lane] : &sm.discard[0][lane];
 
-            // k-steps: each A fragment is re-read from LDS for k-step u + 1
-            // as soon as its two MFMAs of k-step u are issued (the B dequant
-            // latency is covered by the other wave of the SIMD).  The
-            // scheduling barrier at the end of each k-step keeps the compiler
-            // from hoisting work across k-steps (register pressure).
-            h8_t av[MF];
+            // k-step pipeline: the A-operand LDS reads and the B dequant of
+            // k-step u + 1 are issued before the MFMAs of k-step u, so their
+            // latency hides behind those MFMAs.  The scheduling barrier at the
+            // end of each k-step keeps the compiler from hoisting work across
+            // k-steps (register pressure).
+            h8_t bv[kNF], av[MF];
+#pragma unroll
+            for (int f = 0; f < kNF; ++f) bv[f] = dequant8((uint32_t)bq[f][0][0], sbf[f][0]);
 #pragma unroll
             for (int fm = 0; fm < MF; ++fm) av[fm] = sm.a[p].v[fm][kHalfSteps * kh][lane];
 #pragma unroll
             for (int u = 0; u < kHalfSteps; ++u) {
-                h8_t bv[kNF];
+                h8_t nbv[kNF], nav[MF];
+                if (u + 1 < kHalfSteps) {
 #pragma unroll
-                for (int f = 0; f < kNF; ++f) bv[f] = dequant8((uint32_t)bq[f][u >> 2][u & 3], sbf[f][u >> 1]);
-                if (a_store)
-                    sm.a[p ^ 1].v[af][kHalfSteps * ah + u][lane] =
-                        dequant8((uint32_t)aq[u >> 2][u & 3], sa[u >> 1]);
+                    for (int fm = 0; fm < MF; ++fm) nav[fm] = sm.a[p].v[fm][kHalfSteps * kh + u + 1][lane];
 #pragma unroll
-                for (int fm = 0; fm < MF; ++fm) {
+                    for (int f = 0; f < kNF; ++f)
+                        nbv[f] = dequant8((uint32_t)bq[f][(u + 1) >> 2][(u + 1) & 3], sbf[f][(u + 1) >> 1]);
+                }
+#pragma unroll
+                for (int fm = 0; fm < MF; ++fm)
 #pragma unroll
                     for (int f = 0; f < kNF; ++f)
                         part[f][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[f], av[fm], part[f][fm], 0, 0, 0);
-                    if (u + 1 < kHalfSteps) av[fm] = sm.a[p].v[fm][kHalfSteps * kh + u + 1][lane];
-                }
-                // Piece c (k-steps 4c .. 4c+3) of B and of the raw A is now
-                // dequantised in full: fetch the next stage's.
-                if ((u & 3) == 3 && has1) {
+                // Dequantise k-step u of the raw A into LDS (before piece
+                // u / 4 of the raw A is re-loaded below).
+                a_dst[u * kWave] = dequant8((uint32_t)aq[u >> 2][u & 3], sa[u >> 1]);
+                // Piece c (k-steps 4c .. 4c+3) of B is dequantised in full at
+                // u = 4c + 2 (one k-step ahead), that of the raw A at u = 4c + 3:
+                // fetch the next stage's B and stage i + 2's raw A.  The loads
+                // are unconditional (a stage past the chain re-reads the last
+                // one; rows past the tile read other rows or zeros), which
+                // keeps the k-step one scheduling region.
+                if (u == kHalfSteps - 2) {
 #pragma unroll
-                    for (int f = 0; f < kNF; ++f) bq[f][u >> 2] = load16(rB, offB[f] + 16 * (u >> 2), sbyte1);
+                    for (int f = 0; f < kNF; ++f) {
+                        bq[f][0] = load16(rB, offB[f], sbyte_n);
+                        bq[f][1] = load16(rB, offB[f] + 16, sbyte_n);
+                    }
                 }
-                if ((u & 3) == 3 && a_active && has2) aq[u >> 2] = load16(rA, offA + 16 * (u >> 2), sbyte2);
+                if (u == kHalfSteps - 1) {
+                    aq[0] = load16(rA, offA, sbyte_nn);
+                    aq[1] = load16(rA, offA + 16, sbyte_nn);
+                }
+                if (u + 1 < kHalfSteps) {
+#pragma unroll
+                    for (int f = 0; f < kNF; ++f) bv[f] = nbv[f];
+#pragma unroll
+                    for (int fm = 0; fm < MF; ++fm) av[fm] = nav[fm];
+                }
+#if NVFP4_INTERLEAVE
+                // Issue order: each MFMA followed by a share of the VALU work,
+                // so the dequantisation runs while the matrix core is busy.
+#pragma unroll
+                for (int g = 0; g < MF * kNF; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // up to five VALU
+                }
+#endif
                 __builtin_amdgcn_sched_barrier(0);
             }
             lds_barrier();
