@@ -87,6 +87,10 @@ constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lg
 #ifndef NVFP4_INTERLEAVE
 #define NVFP4_INTERLEAVE 1
 #endif
+#ifndef NVFP4_XCD_REMAP
+#define NVFP4_XCD_REMAP 1
+#endif
+constexpr int kXcds = 8;   // XCDs of the chip; workgroups are dealt to them round-robin
 
 static_assert(kTileN == kColGroups * kNF * 32, "each column group owns kNF 32-column fragments");
 static_assert(kMaxFrags == 3, "the kernel instantiates m-blocks of 1, 2 and 3 fragments");
@@ -269,6 +273,20 @@ __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t ba
         }
 }
 
+// The worker index of this workgroup.  Workgroups are dispatched round-robin
+// over the XCDs (workgroup b runs on XCD b % kXcds), each with its own L2;
+// numbering the workers XCD by XCD gives each XCD a contiguous range of the
+// work order, so the tiles that share A rows (same group) or a B strip (same
+// n-block) mostly meet in one L2.
+__device__ __forceinline__ int worker_id(int G)
+{
+    const int b = blockIdx.x;
+#if NVFP4_XCD_REMAP
+    if (G % kXcds == 0) return (b % kXcds) * (G / kXcds) + b / kXcds;
+#endif
+    return b;
+}
+
 // One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
 // stages (one chain for any K <= 8192); first_chain / last_chain place this
@@ -350,7 +368,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const uint32_t wave_in_slot =
         (uint32_t)(cg * kNF + kh) * (kMaxFrags * 4) * (kWave * 16u) + (uint32_t)lane * 16u;
     const uint32_t scratch_base =
-        (uint32_t)scratch_slot(blockIdx.x) * kSlotFloats * 4u + wave_in_slot;
+        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + wave_in_slot;
 
     {
         const int c_begin = s_begin;
@@ -562,7 +580,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         store_c<MF>(sm, ga, m0, n0, own, cg, kh);
         return;
     }
-    const int me = blockIdx.x;
+    const int me = worker_id(args.G);
     const int tile = tile_index(args.sched, pos);
     // Partial tile -> this workgroup's slot (partial_slot).  The stores carry
     // the device-scope coherence bit (sc1), so they are written through past
@@ -600,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
     __shared__ SharedMem sm;
     __shared__ int s_flag;
 
-    const int w = blockIdx.x;
+    const int w = worker_id(args.G);
     const int64_t b1 = boundary(args.W, args.G, w + 1);
     Pos pos = locate(args.sched, args.ngroups, boundary(args.W, args.G, w));
     while (pos.group < args.ngroups && stage_cost(pos, pos.stage) < b1) {
