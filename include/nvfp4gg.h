@@ -31,7 +31,7 @@
  * tile) that the library allocates with hipMalloc on the first call for a
  * (device, stream) pair and keeps, growing it when a later call needs more
  * (that call synchronises the stream first), until the process ends.  At
- * most 3 x (compute units) x 96 KiB of partials plus 4 bytes per tile
+ * most 3 x (compute units) x 192 KiB of partials plus 4 bytes per tile
  * (16 KiB at least).  The counters return to zero at the end of every call,
  * so calls on one stream may follow each other with no reset; calls on
  * different streams use different workspaces.  A call that must allocate is
@@ -47,7 +47,7 @@
  *                            multiple of 16, a NULL or misaligned (16-byte)
  *                            device pointer of a non-empty operand
  *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle: a
- *                            non-empty group with K_i % 256 != 0, an operand
+ *                            non-empty group with K_i % 128 != 0, an operand
  *                            of 2 GiB or more, or M_i * N_i >= 2^31
  *   NVFP4GG_HIP_ERROR    -3  a HIP call (launch, workspace allocation) failed
  * nvfp4_group_gemm_last_error() describes the last failure on this thread.

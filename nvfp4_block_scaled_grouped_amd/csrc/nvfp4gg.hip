@@ -11,7 +11,7 @@
 //     e2m1(code) * e4m3(scale).  That product has at most 6 significant bits
 //     and lies in [2^-10, 2688], so fp16 holds it exactly, and the fp16 x fp16
 //     products inside the MFMA are exact in fp32.  The contraction runs on
-//     v_mfma_f32_32x32x16_f16 with fp32 accumulation.  (CDNA4's block-scaled
+//     v_mfma_f32_16x16x32_f16 with fp32 accumulation.  (CDNA4's block-scaled
 //     f8f6f4 MFMA takes power-of-two E8M0 scales per 32 K; it cannot carry an
 //     E4M3 mantissa per 16 K, and no 8-bit operand format holds a 6-bit
 //     significand.)
@@ -19,30 +19,30 @@
 //     (its scale operand contributes only a power of two, so it is passed
 //     1.0), then v_pk_mul_f16 multiplies by the E4M3 scale converted to fp16
 //     (exact: every E4M3 value is an fp16 value).
-//   * Tile: one workgroup of 8 waves per CU owns up to 96 rows of A_i
-//     (1..3 fragments of 32 rows) x 256 columns of B_i.  Wave w = 4 kh + cg
-//     owns columns [64 cg, 64 cg + 64) for all rows, over K half kh of every
-//     256-K stage.  A is shared: each stage of the tile's A rows is
+//   * Tile: one workgroup of 8 waves per CU owns all rows of A_i (up to 192,
+//     in m-blocks of at most 6 fragments of 32 rows when M_i is larger) x 256
+//     columns of B_i, so every byte of B_i is streamed from memory once per
+//     m-block.  Wave w owns columns [32 w, 32 w + 32) for all rows of the
+//     tile over the whole K.  A is shared: each stage of the tile's A rows is
 //     dequantised once by the workgroup into LDS as fp16, already in MFMA
 //     operand order, and the waves read it with 16-byte LDS loads.  B is
-//     private to a wave: each lane loads its own MFMA operand bytes straight
-//     into registers and dequantises them there, so one dequantised B
-//     fragment feeds up to 3 MFMAs.
+//     private to a wave: the four lanes of a B row load its 64 stage bytes as
+//     one contiguous run straight into registers (kept three stages ahead)
+//     and dequantise them there, so one dequantised B fragment feeds up to 12
+//     MFMAs.
 //   * K order: the sum over K is order-free.  A and B use the same order, so
 //     every pair (a_k, b_k) meets in the same MFMA slot; it is chosen so that
-//     the two lanes holding a row read one contiguous 64-byte run.
-//   * Accumulation: the two K halves of a stage are summed by different
-//     waves into separate fp32 accumulators (two interleaved chains, each at
-//     most 4096 K long), added at the end; this keeps the rounding error of
-//     long K sums small next to outputs near zero.
-//   * Schedule: the work is the list of (tile, stage) units (schedule.h); a
-//     persistent grid of one workgroup per CU takes equal-cost contiguous
-//     ranges of it, so ragged groups fill the chip in one launch.  A tile
-//     whose stages span several workgroups is finished by the last of them
-//     to arrive: each writes its fp32 partial tile to a workspace slot and
-//     bumps the tile's counter; the one that sees all others done sums the
-//     partials in workgroup order (deterministic) and writes C.  No
-//     workgroup ever waits for another.
+//     each lane's 16 loaded bytes serve four k-steps.
+//   * Accumulation: one fp32 chain per output over at most 8192 K of a
+//     workgroup's segment; segments and chains are added in fp32 at the end.
+//   * Schedule: the work is the list of (tile, stage) units (schedule.h) with
+//     measured per-stage costs; a persistent grid of one workgroup per CU
+//     takes equal-cost contiguous ranges of it, so ragged groups fill the
+//     chip in one launch.  A tile whose stages span several workgroups is
+//     finished by the last of them to arrive: each writes its fp32 partial
+//     tile to a workspace slot and bumps the tile's counter; the one that
+//     sees all others done sums the partials in workgroup order
+//     (deterministic) and writes C.  No workgroup ever waits for another.
 //   * Loads are raw buffer loads whose range is the exact operand size, so
 //     rows past M_i or N_i read as zero without branches.
 #include <hip/hip_runtime.h>
@@ -66,18 +66,15 @@ using namespace nvfp4sched;
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
-typedef float f16x_t __attribute__((ext_vector_type(16)));
 typedef int i4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kWaves = 8;                    // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
-constexpr int kNF = 2;                       // 32-column B fragments per wave
-constexpr int kColGroups = 4;                // 64-column groups of the tile
-constexpr int kKSteps = kStageK / 16;        // MFMA k-steps per stage (16 K each: 8 per lane half)
-constexpr int kHalfSteps = kKSteps / 2;      // k-steps of one wave per stage (its K half)
-constexpr int kMaxChainStages = 32;          // stages one fp32 chain accumulates (4096 K per wave)
-constexpr int kSlotFloats = kColGroups * kNF * kMaxFrags * kWave * 16;   // one partial tile
+constexpr int kKSteps = kStageK / 32;        // MFMA k-steps per stage (32 K each)
+constexpr int kMaxAFrags = 2 * kMaxFrags;    // 16-row A fragments of a tile
+constexpr int kMaxChainStages = 64;          // stages one fp32 chain accumulates (8192 K)
+constexpr int kSlotFloats = kWaves * kMaxAFrags * 2 * kWave * 4;   // one partial tile
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
 constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
@@ -87,14 +84,16 @@ constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lg
 #ifndef NVFP4_INTERLEAVE
 #define NVFP4_INTERLEAVE 1
 #endif
+#ifndef NVFP4_RING3
+#define NVFP4_RING3 1
+#endif
 #ifndef NVFP4_XCD_REMAP
 #define NVFP4_XCD_REMAP 1
 #endif
-constexpr int kXcds = 8;   // XCDs of the chip; workgroups are dealt to them round-robin
 
-static_assert(kTileN == kColGroups * kNF * 32, "each column group owns kNF 32-column fragments");
-static_assert(kMaxFrags == 3, "the kernel instantiates m-blocks of 1, 2 and 3 fragments");
-static_assert(kWaves == 2 * kColGroups, "two K halves per column group");
+static_assert(kTileN == kWaves * 32, "each wave owns two 16-column B fragments");
+static_assert(kMaxFrags == 6, "the kernel instantiates m-blocks of 1 to 6 fragments");
+static_assert(kKSteps == 4, "a stage is one 16-byte piece of 4 k-steps per lane");
 
 struct GroupArgs {
     const uint8_t* A;
@@ -153,40 +152,34 @@ __device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 
 
 // LDS image of the dequantised A rows of one stage, in MFMA operand order:
-// [fragment][k-step][lane] x 8 fp16 (64 KB).
+// [16-row fragment][k-step][lane] x 8 fp16 (48 KB).
 struct AStage {
-    h8_t v[kMaxFrags][kKSteps][kWave];
+    h8_t v[kMaxAFrags][kKSteps][kWave];
 };
 
 // The workgroup's LDS: two A stages.  At the end of a segment the same
-// memory first carries the exchange of the two K halves' fp32 fragments
-// ([column group][B fragment][A fragment][quad][lane]) and then the fp16
-// output tile on its way to C (rows padded by 16 bytes against bank
-// conflicts).
+// memory carries the fp16 output tile on its way to C (rows padded by 16
+// bytes against bank conflicts).
 constexpr int kCTileStride = kTileN + 8;   // halves per LDS row of the output tile
 struct SharedMem {
     union {
         AStage a[2];
-        f4_t xch[kColGroups][kNF][kMaxFrags][4][kWave];
         uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
     };
-    // Target of the A-store of waves that have no A fragment in the tile
+    // Target of the A pieces of waves with a unit past the tile's fragments
     // (their writes are discarded), so the k-step needs no branch.
-    h8_t discard[kKSteps / 2][kWave];
+    h8_t discard[kKSteps][kWave];
 };
-static_assert(sizeof(f4_t) * kColGroups * kNF * kMaxFrags * 4 * kWave <= 2 * sizeof(AStage),
-              "the exchange fits in the A buffers");
-static_assert(sizeof(uint16_t) * kMaxFrags * kFragRows * kCTileStride <= 2 * sizeof(AStage),
-              "the output tile fits in the A buffers");
+static_assert(sizeof(SharedMem) <= 160 * 1024, "the LDS of one workgroup fits a CU");
 
 // fp16 round-to-nearest-even (overflow to inf) of 4 floats, packed.
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d)
+__device__ __forceinline__ uint2 pack4(f4_t v)
 {
     uint2 w;
-    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
-          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
-    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)c) |
-          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)d) << 16);
+    w.x = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+    w.y = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+          ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
     return w;
 }
 
@@ -202,33 +195,55 @@ __device__ __forceinline__ void lds_barrier()
 template <int P>
 using Parity = std::integral_constant<int, P>;
 
+// threadIdx.x behind an empty asm: values derived from it are computed where
+// they are used instead of being hoisted out of the persistent loop, which
+// would keep them in registers through the accumulator-heavy epilogue.
+__device__ __forceinline__ int opaque_tid()
+{
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// A zero accumulator written by opaque moves, so the compiler does not keep
+// a zero constant alive across the persistent loop to copy from.
+__device__ __forceinline__ f4_t zero_acc()
+{
+    f4_t z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(v));
+        z[e] = v;
+    }
+    return z;
+}
+
 // The output tile of the workgroup, fp32 -> fp16 (round to nearest even,
 // overflow to inf), written to C through LDS so that every global store is
-// 16 contiguous bytes of a row.  Wave (cg, kh) holds fragment f = kh of
-// column group cg: own[fm] element r of lane (l32, h) is tile row
-// 32 fm + l32, tile column 64 cg + 32 kh + 8 (r / 4) + 4 h + r % 4.
-// Called by every thread of the workgroup; the LDS is free on return.
+// 16 contiguous bytes of a row.  Wave w holds B fragments 2w, 2w + 1 (16
+// columns each): acc[i][f] element r of lane (c16, kq) is tile row
+// 16 i + c16, tile column 32 w + 16 f + 4 kq + r.  Called by every thread
+// of the workgroup; the LDS is free on return.
 template <int MF>
-__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0, const f16x_t* own,
-                                        int cg, int kh)
+__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0,
+                                        const f4_t (*acc)[2], int wave)
 {
-    const int lane = threadIdx.x % kWave;
-    const int l32 = lane & 31, h = lane >> 5;
+    const int tid = opaque_tid();
+    const int lane = tid % kWave;
+    const int c16 = lane & 15, kq = lane >> 4;
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm)
+    for (int i = 0; i < 2 * MF; ++i)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const int col = 64 * cg + 32 * kh + 8 * q4 + 4 * h;
-            *reinterpret_cast<uint2*>(&sm.ctile[32 * fm + l32][col]) =
-                pack4(own[fm][4 * q4], own[fm][4 * q4 + 1], own[fm][4 * q4 + 2], own[fm][4 * q4 + 3]);
-        }
+        for (int f = 0; f < 2; ++f)
+            *reinterpret_cast<uint2*>(&sm.ctile[16 * i + c16][32 * wave + 16 * f + 4 * kq]) = pack4(acc[i][f]);
     lds_barrier();
     const int M = ga.M, N = ga.N;
     const int rows = M - m0 < MF * kFragRows ? M - m0 : MF * kFragRows;
-    const int chunk = threadIdx.x % (kTileN / 8);          // 8 columns = 16 bytes
+    const int chunk = tid % (kTileN / 8);          // 8 columns = 16 bytes
     const int n = n0 + 8 * chunk;
     const bool vec_ok = (N & 7) == 0;
-    for (int r = threadIdx.x / (kTileN / 8); r < rows; r += kThreads / (kTileN / 8)) {
+    for (int r = tid / (kTileN / 8); r < rows; r += kThreads / (kTileN / 8)) {
         if (n >= N) continue;
         const uint4 v = *reinterpret_cast<const uint4*>(&sm.ctile[r][8 * chunk]);
         uint16_t* dst = ga.C + (size_t)(m0 + r) * N + n;
@@ -242,35 +257,38 @@ __device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int 
     lds_barrier();
 }
 
-// One wave's fp32 fragment block of a partial tile (MF x 16 floats per
-// lane) at base, laid out in 1 KB lane-contiguous pieces.
+// One wave's fp32 block of a partial tile (2 MF x 2 x 4 floats per lane) at
+// base, in 1 KB lane-contiguous pieces.
 template <int MF>
-__device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t base, const f16x_t* own)
+__device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t base, const f4_t (*acc)[2])
 {
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm)
+    for (int i = 0; i < 2 * MF; ++i)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(i4_t, f4_t{own[fm][4 * q], own[fm][4 * q + 1], own[fm][4 * q + 2],
-                                              own[fm][4 * q + 3]}),
-                r, base + (uint32_t)(fm * 4 + q) * (kWave * 16u), 0, kCoherent);
+        for (int f = 0; f < 2; ++f)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i4_t, acc[i][f]), r,
+                                                   base + (uint32_t)(2 * i + f) * (kWave * 16u), 0, kCoherent);
 }
 
-// acc (+)= the block stored by store_block at base (assign when first).
+// acc += the block stored by store_block at base, kChunk pieces at a time
+// (the scheduling barrier keeps the loads of later chunks from being
+// hoisted, which bounds the registers in flight).
 template <int MF>
-__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t base, f16x_t* acc, bool first)
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t base, f4_t (*acc)[2])
 {
+    constexpr int kPieces = 4 * MF;
+    constexpr int kChunk = 12;
 #pragma unroll
-    for (int fm = 0; fm < MF; ++fm)
+    for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+        f4_t v[kChunk];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f4_t v = __builtin_bit_cast(
-                f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, base + (uint32_t)(fm * 4 + q) * (kWave * 16u), 0,
-                                                             kCoherent));
+        for (int q = q0; q < q0 + kChunk && q < kPieces; ++q)
+            v[q - q0] = __builtin_bit_cast(
+                f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[fm][4 * q + e] = first ? v[e] : acc[fm][4 * q + e] + v[e];
-        }
+        for (int q = q0; q < q0 + kChunk && q < kPieces; ++q) acc[q >> 1][q & 1] += v[q - q0];
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // The worker index of this workgroup.  Workgroups are dispatched round-robin
@@ -287,46 +305,73 @@ __device__ __forceinline__ int worker_id(int G)
     return b;
 }
 
+// Compiler fences: the asm takes the values as register operands (so they
+// are computed before it) and clobbers memory (so no load or store moves
+// across it).  Placed before a register is re-loaded, they keep the
+// compiler from copying a value whose load is still in flight.
+template <typename T>
+__device__ __forceinline__ void fence_after(const T& v)
+{
+    asm volatile("" ::"v"(v) : "memory");
+}
+
+// The two E4M3 scale bytes at bits [shift, shift + 16) of a dword -> fp16.
+__device__ __forceinline__ h2_t scales2(uint32_t sc, uint32_t shift)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc >> shift, 1.0f, false);
+}
+
 // One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
 // stages (one chain for any K <= 8192); first_chain / last_chain place this
 // chain in its segment.
 //
-// Waves: wave w = 4 kh + cg owns columns [64 cg, 64 cg + 64) of the tile
-// (kNF = 2 fragments of 32) for all MF x 32 rows, over K half kh of every
-// stage (k-steps 8 kh .. 8 kh + 7).  The two K halves are independent fp32
-// chains, added through LDS at the end of the chain: splitting the sum into
-// two interleaved chains halves the magnitude each fp32 accumulator reaches
-// and the number of additions it makes, and capping a chain at 4096 K per
-// wave bounds both.  The chains of one segment meet in the workgroup's
-// scratch slot; the last one finishes the tile.
+// MFMA: v_mfma_f32_16x16x32_f16 with B as the first operand (16 columns of
+// B_i) and A as the second (16 rows of A_i).  Lane (c16, kq) = (lane % 16,
+// lane / 16) supplies column / row c16 and 8 codes of K; it gets back rows
+// 4 kq .. 4 kq + 3 of the first operand's side, i.e. output row c16 and
+// output columns 4 kq .. 4 kq + 3 of the 16 x 16 block.
 //
-// Pipeline, per stage i of a chain:
-//   * B of stage i is in registers, loaded during stage i - 1: each 16-byte
-//     piece is re-loaded with stage i + 1 as soon as its four k-steps are
-//     dequantised.
-//   * A of stage i is in LDS buffer i % 2, dequantised during stage i - 1:
-//     wave w writes fragment w / 2, k-steps 8 (w % 2) .. 8 (w % 2) + 7, one
-//     k-step per k-step of its own MFMA loop, from raw bytes loaded during
-//     stage i - 2.
+// Waves: wave w owns columns [32 w, 32 w + 32) of the tile (B fragments
+// f = 0, 1 of 16 columns) for all 2 MF 16-row A fragments, over the whole K
+// of the chain, so every byte of B is loaded and dequantised once per tile,
+// by one wave, and one dequantised B fragment feeds 2 MF MFMAs.
+//
+// K order within a stage (128 K, 64 bytes of a row; the sum is order-free
+// and A and B use the same order): at k-step v lane (c16, kq) holds the 8
+// codes at K 32 kq + 8 v, i.e. dword v of the 16 bytes [16 kq, +16) of the
+// row's stage bytes, whose scale block is 2 kq + v / 2 (scale bytes
+// 2 (kq % 2), + 1 of dword kq / 2 of the row's 8 stage scale bytes).  So the
+// four lanes of a row read its 64 stage bytes as one contiguous run, and
+// one 16-byte load per B fragment and stage feeds all four k-steps.
+//
+// A: each stage of the tile's 2 MF fragments of 16 rows is dequantised once
+// by the workgroup into LDS, in operand order.  Fragment a belongs to wave
+// a % 8 (its unit a / 8), so a wave has at most two units.
+//
+// Pipeline, per stage i of the chain (register ring slot p = i % kRing):
+//   * B of stage i is in bq[p], bs[p] (loaded kRing stages earlier); it is
+//     re-loaded with stage i + kRing once its last k-step is dequantised.
+//   * A of stage i is in LDS buffer i % 2.  The raw A of stage i + 1 (aq[p],
+//     as[p], loaded kRing stages earlier) is dequantised into the other
+//     buffer, one piece per k-step of the MFMA loop, then re-loaded with
+//     stage i + 1 + kRing.
 //   * One LDS-only barrier ends the stage.
 template <int MF>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
                                             bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
+    constexpr int NA = 2 * MF;   // 16-row A fragments
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform
-    const int cg = wave % kColGroups;
-    const int kh = wave / kColGroups;
-    const int af = wave >> 1;            // A fragment this wave dequantises
-    const int ah = wave & 1;             // and which half of its k-steps
-    const int lane = threadIdx.x % kWave;
-    const int l32 = lane & 31;
-    const int h = lane >> 5;
+    const int tid = opaque_tid();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+    const int lane = tid % kWave;
+    const int c16 = lane & 15;
+    const int kq = lane >> 4;
     const int M = ga.M, N = ga.N, K = ga.K;
     const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
-    const int ncol = pos.nb * kTileN + cg * (kNF * 32);
+    const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 16;
 
@@ -334,180 +379,176 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
+    const uint32_t sshift = 16u * (uint32_t)(kq & 1);   // this lane's scale bytes within a dword
 
-    // K order within a stage (the sum is order-free; A and B use the same
-    // order): k-step j = 8 q + u (K half q, u < 8) feeds lane half h the 8
-    // codes at K 128 q + 64 h + 8 u, i.e. dword u of the 32 bytes
-    // [64 q + 32 h, +32) of the row's stage bytes, whose scale block is
-    // 8 q + 4 h + u / 2.  So the two lanes of a row read one contiguous,
-    // 64-byte aligned run per K half.
-    // B operand of lane (l32, h) in fragment f: row ncol + 32 f + l32, the 32
-    // bytes of its half of K half kh and their 4 scale bytes.
-    uint32_t offB[kNF], offSB[kNF];
+    // B operand of lane (c16, kq) in fragment f: row n0 + 32 wave + 16 f + c16
+    // (rows past N read 0).
+    uint32_t offB[2], offSB[2];
 #pragma unroll
-    for (int f = 0; f < kNF; ++f) {
-        const uint32_t brow = (uint32_t)(ncol + 32 * f + l32);
-        offB[f] = brow * row_bytes + 64u * kh + 32u * h;
-        offSB[f] = brow * row_scales + 8u * kh + 4u * h;
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
+        offB[f] = brow * row_bytes + 16u * kq;
+        offSB[f] = brow * row_scales + 4u * (kq >> 1);
     }
-    // A bytes this lane dequantises: row m0 + 32 af + l32, its half of K half
-    // ah (k-steps 8 ah .. 8 ah + 7).
-    const bool a_active = af < MF;
-    // Waves without a fragment of this tile load (and discard) the rows of
-    // fragment af % MF, which the L1 already fetches for its owner.
-    const uint32_t arow = (uint32_t)(m0 + 32 * (af % MF) + l32);
-    const uint32_t offA = arow * row_bytes + 64u * ah + 32u * h;
-    const uint32_t offSA = arow * row_scales + 8u * ah + 4u * h;
 
-    f16x_t part[kNF][kMaxFrags];
-    f16x_t own[kMaxFrags];   // after a chain: fragment f = kh of this wave's column group, both K halves
+    // This wave's A units: kU = 1 for MF <= 4, else 2 (unit x is fragment
+    // a = w + 8 x).  A unit past the tile's fragments (a >= 2 MF) loads the
+    // rows of fragment a % (2 MF) again (cache hits) and writes the discard
+    // area.
+    constexpr int kU = NA > kWaves ? 2 : 1;
+    // Register ring depth: stage i's loads go out kRing stages ahead.
+    constexpr int kRing = NVFP4_RING3 ? 3 : 2;
+    static_assert(kRing == 2 || kRing == 3, "ring of two or three stages");
+    uint32_t offA[2], offSA[2];
+    h8_t* adst[2];          // k-step 0 of the unit's fragment in LDS buffer 0
+    uint32_t abuf_step[2];  // bytes from buffer 0 to buffer 1 (0 for the discard area)
+#pragma unroll
+    for (int x = 0; x < kU; ++x) {
+        const int a = wave + kWaves * x;
+        const bool real = a < NA;
+        const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);   // rows past M read 0
+        offA[x] = arow * row_bytes + 16u * kq;
+        offSA[x] = arow * row_scales + 4u * (kq >> 1);
+        adst[x] = real ? &sm.a[0].v[a][0][lane] : &sm.discard[0][lane];
+        abuf_step[x] = real ? (uint32_t)sizeof(AStage) : 0u;
+    }
+
+    f4_t acc[NA][2];
     const __amdgpu_buffer_rsrc_t rP =
         make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
-    // This wave's block of a slot: [column group][B fragment] blocks of
-    // kMaxFrags x 4 x 1 KB; wave (cg, kh) owns block (cg, kh).
-    const uint32_t wave_in_slot =
-        (uint32_t)(cg * kNF + kh) * (kMaxFrags * 4) * (kWave * 16u) + (uint32_t)lane * 16u;
-    const uint32_t scratch_base =
-        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + wave_in_slot;
 
     {
-        const int c_begin = s_begin;
         const int n = s_end - s_begin;
+        // Stage offsets (wave-uniform, in SGPRs); stages past the chain
+        // re-read its last stage, so every load is unconditional and in range.
+        auto sbyte = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
+        };
+        auto sscale = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 16));
+        };
 
-        // Register stage buffers, each one stage ahead of its use: B of the
-        // stage being multiplied (each 16-byte piece re-loaded with the next
-        // stage's as soon as its four k-steps are dequantised), and the raw A
-        // of the stage being dequantised into LDS (likewise re-loaded with
-        // the stage after).
-        i4_t bq[kNF][2];
-        uint32_t bs[kNF];
-        i4_t aq[2] = {i4_t{}, i4_t{}};
-        uint32_t as = 0u;
+        i4_t bq[kRing][2];
+        uint32_t bs[kRing][2];
+        i4_t aq[kRing][2];
+        uint32_t as[kRing][2];
 
-        // Prologue: B of stage 0 and A of stages 0 and 1 in flight; stage 0
-        // of A into LDS buffer 0.
+        // Prologue: raw A of stage 0, then ring slot j < kRing (B of stage j,
+        // raw A of stage j + 1), in the order the stages issue their loads;
+        // stage 0 of A into LDS buffer 0.
         {
-            const uint32_t sbyte = __builtin_amdgcn_readfirstlane(c_begin * (kStageK / 2));
-            const uint32_t sscale = __builtin_amdgcn_readfirstlane(c_begin * (kStageK / 16));
-            i4_t a0[2] = {i4_t{}, i4_t{}};
-            uint32_t as0 = 0u;
-            if (a_active) {
-                a0[0] = load16(rA, offA, sbyte);
-                a0[1] = load16(rA, offA + 16, sbyte);
-                as0 = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale, 0);
+            i4_t a0[2];
+            uint32_t as0[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                a0[x] = load16(rA, offA[x], sbyte(0));
+                as0[x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], sscale(0), 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < kRing; ++j) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f)
+                    bs[j][f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale(j), 0);
+#pragma unroll
+                for (int x = 0; x < kU; ++x)
+                    as[j][x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], sscale(j + 1), 0);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int f = 0; f < 2; ++f) bq[j][f] = load16(rB, offB[f], sbyte(j));
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int x = 0; x < kU; ++x) aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int f = 0; f < kNF; ++f) {
-                bq[f][0] = load16(rB, offB[f], sbyte);
-                bq[f][1] = load16(rB, offB[f] + 16, sbyte);
-                bs[f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale, 0);
-            }
-            if (a_active && n > 1) {
-                aq[0] = load16(rA, offA, sbyte + kStageK / 2);
-                aq[1] = load16(rA, offA + 16, sbyte + kStageK / 2);
-                as = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale + kStageK / 16, 0);
-            }
-            if (a_active) {
-                _Float16 sa[4];
-                scales4(as0, sa);
+            for (int x = 0; x < kU; ++x) {
+                const h2_t sa = scales2(as0[x], sshift);
 #pragma unroll
-                for (int u = 0; u < kHalfSteps; ++u)
-                    sm.a[0].v[af][kHalfSteps * ah + u][lane] = dequant8((uint32_t)a0[u >> 2][u & 3], sa[u >> 1]);
+                for (int v = 0; v < kKSteps; ++v) adst[x][v * kWave] = dequant8((uint32_t)a0[x][v], sa[v >> 1]);
             }
         }
 #pragma unroll
-        for (int f = 0; f < kNF; ++f)
+        for (int i = 0; i < NA; ++i)
 #pragma unroll
-            for (int fm = 0; fm < MF; ++fm) part[f][fm] = f16x_t{};
+            for (int f = 0; f < 2; ++f) acc[i][f] = zero_acc();
         lds_barrier();
 
         auto stage = [&](auto parity, int i) {
             constexpr int p = decltype(parity)::value;
-            const bool has1 = i + 1 < n;
-            const bool has2 = i + 2 < n;
-            // Stage offsets are wave-uniform; readfirstlane keeps them in
-            // SGPRs (the buffer loads' soffset) where the compiler would
-            // otherwise not prove it.
-            const uint32_t sbyte1 = __builtin_amdgcn_readfirstlane((c_begin + i + 1) * (kStageK / 2));
-            const uint32_t sscale1 = __builtin_amdgcn_readfirstlane((c_begin + i + 1) * (kStageK / 16));
-            const uint32_t sbyte2 = sbyte1 + kStageK / 2;
-            const uint32_t sscale2 = sscale1 + kStageK / 16;
-            const uint32_t sbyte_n = has1 ? sbyte1 : sbyte1 - kStageK / 2;    // B loads: next stage, or this one
-            const uint32_t sbyte_nn = has2 ? sbyte2 : sbyte1 - kStageK / 2;   // A loads: stage i + 2, or this one
+            const uint32_t sb2 = sbyte(i + kRing), ss2 = sscale(i + kRing);
+            const uint32_t sb3 = sbyte(i + 1 + kRing), ss3 = sscale(i + 1 + kRing);
+            // LDS A buffers: this stage reads buffer i % 2 and writes the other.
+            const int lb = i & 1;
+            const AStage& ard = sm.a[lb];
+            h8_t* awr[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x)
+                awr[x] = reinterpret_cast<h8_t*>(reinterpret_cast<char*>(adst[x]) + (lb ^ 1) * abuf_step[x]);
+            // Scales of this stage (B) and of the A being dequantised
+            // (stage i + 1), converted before their registers are re-loaded.
+            const h2_t sbf[2] = {scales2(bs[p][0], sshift), scales2(bs[p][1], sshift)};
+            h2_t saf[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x) saf[x] = scales2(as[p][x], sshift);
+            fence_after(sbf[0]);
+            fence_after(sbf[1]);
+#pragma unroll
+            for (int x = 0; x < kU; ++x) fence_after(saf[x]);
+#pragma unroll
+            for (int f = 0; f < 2; ++f) bs[p][f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], ss2, 0);
+#pragma unroll
+            for (int x = 0; x < kU; ++x) as[p][x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], ss3, 0);
 
-            _Float16 sbf[kNF][4];
+            // k-step pipeline: the B dequant of k-step v + 1 is issued before
+            // the MFMAs of k-step v; the scheduling barrier at the end of each
+            // k-step keeps the compiler from hoisting work across k-steps.
+            h8_t bv[2] = {dequant8((uint32_t)bq[p][0][0], sbf[0][0]), dequant8((uint32_t)bq[p][1][0], sbf[1][0])};
 #pragma unroll
-            for (int f = 0; f < kNF; ++f) scales4(bs[f], sbf[f]);
-            _Float16 sa[4];
-            scales4(as, sa);
-            if (has1) {
+            for (int v = 0; v < kKSteps; ++v) {
+                h8_t av[NA];
 #pragma unroll
-                for (int f = 0; f < kNF; ++f) bs[f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale1, 0);
-            }
-            if (a_active && has2) as = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA, sscale2, 0);
-            // Where this wave's A dequantisation goes: its fragment of the
-            // next stage's buffer, or the discard area.  (In a chain's last
-            // stage the next buffer is written but never read.)
-            h8_t* const a_dst = a_active ? &sm.a[p ^ 1].v[af][kHalfSteps * ah][lane] : &sm.discard[0][lane];
-
-            // k-step pipeline: the A-operand LDS reads and the B dequant of
-            // k-step u + 1 are issued before the MFMAs of k-step u, so their
-            // latency hides behind those MFMAs.  The scheduling barrier at the
-            // end of each k-step keeps the compiler from hoisting work across
-            // k-steps (register pressure).
-            h8_t bv[kNF], av[MF];
+                for (int a = 0; a < NA; ++a) av[a] = ard.v[a][v][lane];
+                h8_t nbv[2] = {bv[0], bv[1]};
+                if (v + 1 < kKSteps) {
 #pragma unroll
-            for (int f = 0; f < kNF; ++f) bv[f] = dequant8((uint32_t)bq[f][0][0], sbf[f][0]);
-#pragma unroll
-            for (int fm = 0; fm < MF; ++fm) av[fm] = sm.a[p].v[fm][kHalfSteps * kh][lane];
-#pragma unroll
-            for (int u = 0; u < kHalfSteps; ++u) {
-                h8_t nbv[kNF], nav[MF];
-                if (u + 1 < kHalfSteps) {
-#pragma unroll
-                    for (int fm = 0; fm < MF; ++fm) nav[fm] = sm.a[p].v[fm][kHalfSteps * kh + u + 1][lane];
-#pragma unroll
-                    for (int f = 0; f < kNF; ++f)
-                        nbv[f] = dequant8((uint32_t)bq[f][(u + 1) >> 2][(u + 1) & 3], sbf[f][(u + 1) >> 1]);
+                    for (int f = 0; f < 2; ++f)
+                        nbv[f] = dequant8((uint32_t)bq[p][f][v + 1], sbf[f][(v + 1) >> 1]);
                 }
 #pragma unroll
-                for (int fm = 0; fm < MF; ++fm)
+                for (int a = 0; a < NA; ++a)
 #pragma unroll
-                    for (int f = 0; f < kNF; ++f)
-                        part[f][fm] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[f], av[fm], part[f][fm], 0, 0, 0);
-                // Dequantise k-step u of the raw A into LDS (before piece
-                // u / 4 of the raw A is re-loaded below).
-                a_dst[u * kWave] = dequant8((uint32_t)aq[u >> 2][u & 3], sa[u >> 1]);
-                // Piece c (k-steps 4c .. 4c+3) of B is dequantised in full at
-                // u = 4c + 2 (one k-step ahead), that of the raw A at u = 4c + 3:
-                // fetch the next stage's B and stage i + 2's raw A.  The loads
-                // are unconditional (a stage past the chain re-reads the last
-                // one; rows past the tile read other rows or zeros), which
-                // keeps the k-step one scheduling region.
-                if (u == kHalfSteps - 2) {
+                    for (int f = 0; f < 2; ++f)
+                        acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[f], av[a], acc[a][f], 0, 0, 0);
+                // Piece v of each A unit of stage i + 1 -> the other LDS buffer.
 #pragma unroll
-                    for (int f = 0; f < kNF; ++f) {
-                        bq[f][0] = load16(rB, offB[f], sbyte_n);
-                        bq[f][1] = load16(rB, offB[f] + 16, sbyte_n);
-                    }
+                for (int x = 0; x < kU; ++x)
+                    awr[x][v * kWave] = dequant8((uint32_t)aq[p][x][v], saf[x][v >> 1]);
+                if (v == kKSteps - 2) {
+                    // B is fully dequantised (the last k-step is in nbv).
+                    fence_after(nbv[0]);
+                    fence_after(nbv[1]);
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) bq[p][f] = load16(rB, offB[f], sb2);
                 }
-                if (u == kHalfSteps - 1) {
-                    aq[0] = load16(rA, offA, sbyte_nn);
-                    aq[1] = load16(rA, offA + 16, sbyte_nn);
-                }
-                if (u + 1 < kHalfSteps) {
+                if (v == kKSteps - 1) {
+                    asm volatile("" ::: "memory");
 #pragma unroll
-                    for (int f = 0; f < kNF; ++f) bv[f] = nbv[f];
-#pragma unroll
-                    for (int fm = 0; fm < MF; ++fm) av[fm] = nav[fm];
+                    for (int x = 0; x < kU; ++x) aq[p][x] = load16(rA, offA[x], sb3);
                 }
+                bv[0] = nbv[0];
+                bv[1] = nbv[1];
 #if NVFP4_INTERLEAVE
-                // Issue order: each MFMA followed by a share of the VALU work,
-                // so the dequantisation runs while the matrix core is busy.
+                // Issue order: the A operands are read from LDS a few MFMAs
+                // ahead of their use (so few are live at once), and the MFMAs
+                // alternate with the VALU work, so the dequantisation runs
+                // while the matrix core is busy.
+                __builtin_amdgcn_sched_group_barrier(0x100, NA < 2 ? NA : 2, 0);   // LDS reads
 #pragma unroll
-                for (int g = 0; g < MF * kNF; ++g) {
+                for (int g = 0; g < 2 * NA; ++g) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // up to five VALU
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // up to two VALU
+                    if ((g & 1) && (g >> 1) + 2 < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
 #endif
                 __builtin_amdgcn_sched_barrier(0);
@@ -515,81 +556,50 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             lds_barrier();
         };
 
-        for (int i = 0; i < n; i += 2) {
+        int i = 0;
+        for (; i + kRing - 1 < n; i += kRing) {
             stage(Parity<0>{}, i);
-            if (i + 1 >= n) break;
             stage(Parity<1>{}, i + 1);
+            if constexpr (kRing > 2) stage(Parity<2>{}, i + 2);
         }
-
-        // Add the two K halves through LDS (the A buffers are free: every
-        // wave is past the last stage's barrier).  Wave (cg, kh) hands
-        // fragment 1 - kh to its partner (cg, 1 - kh) and keeps fragment kh,
-        // so both halves of the workgroup carry the epilogue.  The indices
-        // are spelled out per kh to keep the register arrays statically
-        // indexed.
-        if (kh == 0) {
-#pragma unroll
-            for (int fm = 0; fm < MF; ++fm)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sm.xch[cg][1][fm][q][lane] = f4_t{part[1][fm][4 * q], part[1][fm][4 * q + 1],
-                                                      part[1][fm][4 * q + 2], part[1][fm][4 * q + 3]};
-        } else {
-#pragma unroll
-            for (int fm = 0; fm < MF; ++fm)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    sm.xch[cg][0][fm][q][lane] = f4_t{part[0][fm][4 * q], part[0][fm][4 * q + 1],
-                                                      part[0][fm][4 * q + 2], part[0][fm][4 * q + 3]};
-        }
-        lds_barrier();
-        if (kh == 0) {
-#pragma unroll
-            for (int fm = 0; fm < MF; ++fm) own[fm] = part[0][fm];
-        } else {
-#pragma unroll
-            for (int fm = 0; fm < MF; ++fm) own[fm] = part[1][fm];
-        }
-#pragma unroll
-        for (int fm = 0; fm < MF; ++fm)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f4_t v = sm.xch[cg][kh][fm][q][lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) own[fm][4 * q + e] += v[e];
-            }
-        lds_barrier();   // the exchange is read before anything else is written to the LDS
+        if (i < n) stage(Parity<0>{}, i);
+        if (kRing > 2 && i + 1 < n) stage(Parity<1>{}, i + 1);
     }
+    // Epilogue addresses, recomputed here rather than kept through the loop.
+    const uint32_t ewave_in_slot =
+        (uint32_t)wave * (kMaxAFrags * 2) * (kWave * 16u) + (uint32_t)(opaque_tid() % kWave) * 16u;
+    const uint32_t scratch_base =
+        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + ewave_in_slot;
     // Chains of one segment meet in the scratch slot.
-    if (!first_chain) load_block<MF>(rP, scratch_base, own, false);
+    if (!first_chain) load_block<MF>(rP, scratch_base, acc);
     if (!last_chain) {
-        store_block<MF>(rP, scratch_base, own);
+        store_block<MF>(rP, scratch_base, acc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         return;
     }
 
     // Finish the tile: alone, or as one of several contributors.  Every
-    // wave holds its fragment of the segment's sum in own.
-    const int unit = unit_cost(pos.frags);
+    // wave holds its part of the segment's sum in acc.
+    const int unit = pos.unit;
     const int64_t c_first = pos.tile_cost0;
     const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
-    const int w_first = owner(args.W, args.G, c_first);
-    const int w_last = owner(args.W, args.G, c_last);
-    const int n0 = pos.nb * kTileN;
+    const int w_first = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_first));
+    const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
     if (w_first == w_last) {
-        store_c<MF>(sm, ga, m0, n0, own, cg, kh);
+        asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
         return;
     }
-    const int me = worker_id(args.G);
+    const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
     const int tile = tile_index(args.sched, pos);
     // Partial tile -> this workgroup's slot (partial_slot).  The stores carry
     // the device-scope coherence bit (sc1), so they are written through past
     // this XCD's L2; waiting for them before the counter update publishes
     // them to whichever workgroup finishes the tile, with no cache flush.
     auto slot_base = [&](int w) {
-        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + wave_in_slot;
+        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + ewave_in_slot;
     };
-    store_block<MF>(rP, slot_base(me), own);
+    store_block<MF>(rP, slot_base(me), acc);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -598,19 +608,51 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         *s_flag = (old == w_last - w_first) ? 1 : 0;
     }
     __syncthreads();
-    const bool last = *s_flag != 0;
+    const bool last = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
     __syncthreads();   // s_flag is reused by the next segment
     if (!last) return;
     // Sum the contributors' partials in workgroup order, so the result does
     // not depend on who arrived last.  When this workgroup is the first
-    // contributor its partial is still in registers; otherwise it is read
-    // back like the others.  The loads carry the device-scope coherence bit
-    // as well.
-    for (int w = me == w_first ? w_first + 1 : w_first; w <= w_last; ++w)
-        load_block<MF>(rP, slot_base(w), own, w == w_first);
-    store_c<MF>(sm, ga, m0, n0, own, cg, kh);
+    // contributor its partial is still in registers; otherwise the sum
+    // starts from zero and every partial, its own included, is read back.
+    // (A select rather than a branch, so there is one copy of the
+    // accumulators.)  The loads carry the device-scope coherence bit as well.
+    const bool keep = me == w_first;
+#pragma unroll
+    for (int a = 0; a < 2 * MF; ++a)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[a][f][e] = keep ? acc[a][f][e] : 0.0f;
+    for (int w = keep ? w_first + 1 : w_first; w <= w_last; ++w) load_block<MF>(rP, slot_base(w), acc);
+    asm volatile("; fix-up" ::: "memory");
+    store_c<MF>(sm, ga, m0, n0, acc, wave);
     if (threadIdx.x == 0)
         __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-uniform values computed in vector registers (64-bit divisions have
+// no scalar form) moved back to scalar registers, so they do not occupy
+// vector registers through the whole loop.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v)
+{
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ Pos uniform(const Pos& p)
+{
+    Pos r;
+    r.group = uniform(p.group);
+    r.nb = uniform(p.nb);
+    r.mb = uniform(p.mb);
+    r.stage = uniform(p.stage);
+    r.frags = uniform(p.frags);
+    r.unit = uniform(p.unit);
+    r.tile_cost0 = uniform(p.tile_cost0);
+    return r;
 }
 
 __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
@@ -618,14 +660,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
     __shared__ SharedMem sm;
     __shared__ int s_flag;
 
-    const int w = worker_id(args.G);
-    const int64_t b1 = boundary(args.W, args.G, w + 1);
-    Pos pos = locate(args.sched, args.ngroups, boundary(args.W, args.G, w));
+    const int w = uniform(worker_id(args.G));
+    const int64_t b1 = uniform(boundary(args.W, args.G, w + 1));
+    Pos pos = uniform(locate(args.sched, args.ngroups, uniform(boundary(args.W, args.G, w))));
     while (pos.group < args.ngroups && stage_cost(pos, pos.stage) < b1) {
         const GroupSched& gs = args.sched[pos.group];
-        const int unit = unit_cost(pos.frags);
+        const int unit = pos.unit;
         // Stages of this tile that start before b1.
-        const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
+        const int64_t s_end64 = uniform((int64_t)((b1 - pos.tile_cost0 + unit - 1) / unit));
         const int s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
         // The segment runs as chains of at most kMaxChainStages stages.
         for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
@@ -634,11 +676,14 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
             switch (pos.frags) {
                 case 1: run_segment<1>(args, pos, c0, c1, first, last, sm, &s_flag); break;
                 case 2: run_segment<2>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                default: run_segment<3>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                case 3: run_segment<3>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                case 4: run_segment<4>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                case 5: run_segment<5>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+                default: run_segment<6>(args, pos, c0, c1, first, last, sm, &s_flag); break;
             }
         }
         if (s_end < gs.stages) break;
-        pos = locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages);
+        pos = uniform(locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages));
     }
 }
 
@@ -691,11 +736,6 @@ int fail(int code, const std::string& msg)
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
-
-// Minimum cost handed to one workgroup: keeps every workgroup range longer
-// than the costliest stage, which the fixup relies on.
-constexpr int64_t kMinUnitsPerWG = 8;
-static_assert(kMinUnitsPerWG >= kMaxFrags + kStageFixedCost, "a workgroup range must hold a stage");
 
 // Workspace of the split-tile fixup, one per (device, stream): three
 // partial-tile slots per workgroup and the per-tile counters (zero between calls; the last contributor
@@ -786,7 +826,7 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
             if (!p || !aligned16(p))
                 return fail(NVFP4GG_INVALID_ARG, gs + "an operand pointer is NULL or not 16-byte aligned");
         if (K[i] % kStageK != 0)
-            return fail(NVFP4GG_UNSUPPORTED, gs + "this kernel needs K % 256 == 0");
+            return fail(NVFP4GG_UNSUPPORTED, gs + "this kernel needs K % 128 == 0");
         // Byte offsets of the buffer loads are 32-bit and may run one tile
         // past the last row.
         const int64_t rows = (int64_t)(M[i] > N[i] ? M[i] : N[i]) + kTileN;
@@ -837,22 +877,14 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
             ga.M = M[gi];
             ga.N = N[gi];
             ga.K = K[gi];
-            sc.frags = ceil_div(M[gi], kFragRows);
-            sc.mblocks = ceil_div(sc.frags, kMaxFrags);
-            sc.nblocks = ceil_div(N[gi], kTileN);
-            sc.stages = K[gi] / kStageK;
-            sc.cost_begin = cost;
-            sc.tile_begin = tiles;
+            sc = make_group_sched(M[gi], N[gi], K[gi], cost, tiles);
             cost += group_cost(sc);
             tiles += sc.mblocks * sc.nblocks;
         }
         if (n == 0) continue;
         args.ngroups = n;
         args.W = cost;
-        int64_t G = cost / kMinUnitsPerWG;
-        if (G > cus) G = cus;
-        if (G < 1) G = 1;
-        args.G = (int)G;
+        args.G = grid_size(cost, cus);
         Workspace ws;
         const int rc = get_workspace(dev, s, args.G, tiles, ws);
         if (rc != NVFP4GG_OK) return rc;

@@ -15,20 +15,14 @@ using namespace nvfp4sched;
 static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { ++fails; std::printf("FAIL %s:%d: ", __FILE__, __LINE__); std::printf(__VA_ARGS__); std::printf("\n"); return; } } while (0)
 
-static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus,
-                     int64_t min_units)
+static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus)
 {
     int ng = (int)M.size();
     GroupSched gs[kMaxGroups];
     int64_t cost = 0;
     int tiles = 0;
     for (int i = 0; i < ng; ++i) {
-        gs[i].frags = ceil_div_i(M[i], kFragRows);
-        gs[i].mblocks = ceil_div_i(gs[i].frags, kMaxFrags);
-        gs[i].nblocks = ceil_div_i(N[i], kTileN);
-        gs[i].stages = K[i] / kStageK;
-        gs[i].cost_begin = cost;
-        gs[i].tile_begin = tiles;
+        gs[i] = make_group_sched(M[i], N[i], K[i], cost, tiles);
         cost += group_cost(gs[i]);
         tiles += gs[i].mblocks * gs[i].nblocks;
         // m-block partition covers all fragments, each block 1..kMaxFrags
@@ -40,12 +34,18 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
             sum += f;
         }
         CHECK(sum == gs[i].frags, "frag sum");
+        // the closed-form m-block cost prefix matches the sum of its tiles
+        int64_t c = 0;
+        for (int b = 0; b <= gs[i].mblocks; ++b) {
+            CHECK(mblock_cost0(gs[i], b) == c, "mblock_cost0 group %d block %d", i, b);
+            if (b < gs[i].mblocks)
+                c += kTileCost + (int64_t)gs[i].stages * unit_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b));
+        }
     }
     const int64_t W = cost;
-    int64_t G64 = W / min_units;
-    if (G64 > cus) G64 = cus;
-    if (G64 < 1) G64 = 1;
-    const int G = (int)G64;
+    const int G = grid_size(W, cus);
+    CHECK(G >= 1 && G <= cus, "grid size %d", G);
+    CHECK(G == 1 || W / G >= kMinUnitsPerWG, "workgroup range shorter than kMinUnitsPerWG");
     // covered[(tile, stage)] = workgroup
     std::map<std::pair<int, int>, int> covered;
     std::map<int, std::set<int>> contrib;         // tile -> workgroups
@@ -57,7 +57,8 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
         while (pos.group < ng && stage_cost(pos, pos.stage) < b1) {
             CHECK(++guard < 1000000, "runaway walk");
             const GroupSched& g = gs[pos.group];
-            const int unit = unit_cost(pos.frags);
+            const int unit = pos.unit;
+            CHECK(unit == unit_cost(pos.frags), "unit cost");
             const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
             const int s_end = s_end64 < g.stages ? (int)s_end64 : g.stages;
             CHECK(s_end > pos.stage, "empty segment w=%d", w);
@@ -102,11 +103,11 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
 int main()
 {
     // The five workloads.
-    run_case({64, 96}, {256, 256}, {512, 512}, 256, 8);
-    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256, 8);
-    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256, 8);
-    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256, 8);
-    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256, 8);
+    run_case({64, 96}, {256, 256}, {512, 512}, 256);
+    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256);
+    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256);
+    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256);
+    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256);
     // Random shapes and grid sizes.
     std::mt19937 rng(12345);
     for (int it = 0; it < 3000; ++it) {
@@ -115,9 +116,9 @@ int main()
         for (int i = 0; i < ng; ++i) {
             M.push_back(1 + rng() % 700);
             N.push_back(1 + rng() % 3000);
-            K.push_back(256 * (1 + rng() % 12));
+            K.push_back(kStageK * (1 + rng() % 24));
         }
-        run_case(M, N, K, 1 + rng() % 300, kMaxFrags + kStageFixedCost + rng() % 40);
+        run_case(M, N, K, 1 + rng() % 300);
         if (fails) break;
     }
     if (fails) { std::printf("FAILED %d\n", fails); return 1; }

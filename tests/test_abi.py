@@ -87,8 +87,8 @@ def test_second_group_is_validated(lib):
 
 
 def test_unsupported_k(lib):
-    assert _call([8], [8], [272]) == nv.UNSUPPORTED
-    assert "K % 256" in nv.last_error()
+    assert _call([8], [8], [144]) == nv.UNSUPPORTED
+    assert "K % 128" in nv.last_error()
 
 
 def test_unsupported_huge_operand(lib):

@@ -116,6 +116,7 @@ def test_config1_full(nv, oracle_lib):
     ([64, 65, 130], [256, 257, 259], [256, 512, 256]),
     ([200], [300], [1792]),
     ([5, 0, 7], [9, 11, 0], [256, 256, 256]),
+    ([385, 129, 192], [520, 260, 33], [384, 640, 128]),
 ])
 def test_ragged_shapes(nv, oracle_lib, M, N, K):
     _full_parity(nv, oracle_lib, M, N, K, seed=21)
@@ -199,9 +200,9 @@ def test_workload_sampled(nv, oracle_lib, cfg):
 
 
 def test_long_segments_run_as_several_chains(nv, oracle_lib):
-    """K = 17408 (68 stages) over 128 column blocks: every workgroup's range
-    covers more than 32 stages of a tile, so its segment runs as two chains
-    that meet in the scratch slot.  Checked on sampled elements."""
+    """K = 17408 (136 stages of 128) over 128 column blocks: a workgroup's
+    range covers more than 64 stages of a tile, so its segment runs as two
+    chains that meet in the scratch slot.  Checked on sampled elements."""
     M, N, K = [96], [32768], [17408]
     _say("long segments M=%s N=%s K=%s" % (M, N, K))
     A, B, SA, SB = workloads.make_inputs(M, N, K, 31)
