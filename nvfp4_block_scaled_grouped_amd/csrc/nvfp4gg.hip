@@ -543,12 +543,13 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
                 // ahead of their use (so few are live at once), and the MFMAs
                 // alternate with the VALU work, so the dequantisation runs
                 // while the matrix core is busy.
-                __builtin_amdgcn_sched_group_barrier(0x100, NA < 2 ? NA : 2, 0);   // LDS reads
+                constexpr int kLead = NA <= 8 ? NA : 8;   // A operands read ahead of their MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);   // LDS reads
 #pragma unroll
                 for (int g = 0; g < 2 * NA; ++g) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
                     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // up to two VALU
-                    if ((g & 1) && (g >> 1) + 2 < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if ((g & 1) && (g >> 1) + kLead < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
 #endif
                 __builtin_amdgcn_sched_barrier(0);
