@@ -169,6 +169,12 @@ struct SharedMem {
     // Target of the A pieces of waves with a unit past the tile's fragments
     // (their writes are discarded), so the k-step needs no branch.
     h8_t discard[kKSteps][kWave];
+    // Per-wave staging of the scale bytes of 4 stages (two blocks in
+    // flight): rows 0..31 are the wave's B rows, rows 32 + 16 x .. are its
+    // A unit x's rows; 8 dwords per row (4 stages x 8 scale bytes).  A wave
+    // loads a block with one 16-byte load per lane and redistributes it to
+    // the lanes that need each dword through its own rows of this array.
+    uint32_t sscr[2][kWaves][64][8];
 };
 static_assert(sizeof(SharedMem) <= 160 * 1024, "the LDS of one workgroup fits a CU");
 
@@ -383,12 +389,11 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 
     // B operand of lane (c16, kq) in fragment f: row n0 + 32 wave + 16 f + c16
     // (rows past N read 0).
-    uint32_t offB[2], offSB[2];
+    uint32_t offB[2];
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
         offB[f] = brow * row_bytes + 16u * kq;
-        offSB[f] = brow * row_scales + 4u * (kq >> 1);
     }
 
     // This wave's A units: kU = 1 for MF <= 4, else 2 (unit x is fragment
@@ -397,9 +402,9 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     // area.
     constexpr int kU = NA > kWaves ? 2 : 1;
     // Register ring depth: stage i's loads go out kRing stages ahead.
-    constexpr int kRing = NVFP4_RING3 ? 3 : 2;
+    constexpr int kRing = NVFP4_RING3 && MF <= 4 ? 3 : 2;
     static_assert(kRing == 2 || kRing == 3, "ring of two or three stages");
-    uint32_t offA[2], offSA[2];
+    uint32_t offA[2];
     h8_t* adst[2];          // k-step 0 of the unit's fragment in LDS buffer 0
     uint32_t abuf_step[2];  // bytes from buffer 0 to buffer 1 (0 for the discard area)
 #pragma unroll
@@ -408,7 +413,6 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         const bool real = a < NA;
         const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);   // rows past M read 0
         offA[x] = arow * row_bytes + 16u * kq;
-        offSA[x] = arow * row_scales + 4u * (kq >> 1);
         adst[x] = real ? &sm.a[0].v[a][0][lane] : &sm.discard[0][lane];
         abuf_step[x] = real ? (uint32_t)sizeof(AStage) : 0u;
     }
@@ -424,36 +428,61 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         auto sbyte = [&](int t) {
             return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
         };
-        auto sscale = [&](int t) {
-            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 16));
-        };
 
         i4_t bq[kRing][2];
-        uint32_t bs[kRing][2];
         i4_t aq[kRing][2];
-        uint32_t as[kRing][2];
+
+        // Scale staging: lane L loads 16 bytes (2 stages) of the scale row
+        // L / 2 of the wave (B rows, then each A unit's 16 rows) for a block of
+        // 4 stages, and writes them to its rows of sm.sscr.  Only the wave
+        // itself reads its rows, and a wave's LDS accesses complete in issue
+        // order, so no barrier guards them.  A block that runs past the end
+        // of K reads the next row's bytes or, past the buffer, zeros; the
+        // stages that use them do not exist.
+        const int slane = lane;
+        const uint32_t offSBs = (uint32_t)(n0 + 32 * wave + (slane >> 1)) * row_scales + 16u * (slane & 1);
+        uint32_t offSAs[2];
+#pragma unroll
+        for (int x = 0; x < kU; ++x) {
+            const int a = wave + kWaves * x;
+            offSAs[x] = (uint32_t)(m0 + 16 * (a % NA) + ((slane >> 1) & 15)) * row_scales + 16u * (slane & 1);
+        }
+        auto sblock = [&](int b) {   // scale byte offset of the block starting at stage b of the chain
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (kStageK / 16));
+        };
+        i4_t sregB, sregA[2];
+        auto scale_load = [&](int b) {
+            sregB = load16(rSB, offSBs, sblock(b));
+#pragma unroll
+            for (int x = 0; x < kU; ++x) sregA[x] = load16(rSA, offSAs[x], sblock(b));
+        };
+        auto scale_store = [&](int buf) {
+            *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][slane >> 1][4 * (slane & 1)]) = sregB;
+#pragma unroll
+            for (int x = 0; x < kU; ++x)
+                *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][32 + 16 * x + ((slane >> 1) & 15)][4 * (slane & 1)]) =
+                    sregA[x];
+        };
+        // The scale dword of this lane for stage t of the chain: B fragment f,
+        // or A unit x.
+        auto scale_b = [&](int t, int f) {
+            return sm.sscr[(t >> 2) & 1][wave][16 * f + c16][2 * (t & 3) + (kq >> 1)];
+        };
+        auto scale_a = [&](int t, int x) {
+            return sm.sscr[(t >> 2) & 1][wave][32 + 16 * x + c16][2 * (t & 3) + (kq >> 1)];
+        };
 
         // Prologue: raw A of stage 0, then ring slot j < kRing (B of stage j,
         // raw A of stage j + 1), in the order the stages issue their loads;
         // stage 0 of A into LDS buffer 0.
         {
             i4_t a0[2];
-            uint32_t as0[2];
+            scale_load(0);
 #pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                a0[x] = load16(rA, offA[x], sbyte(0));
-                as0[x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], sscale(0), 0);
-            }
+            for (int x = 0; x < kU; ++x) a0[x] = load16(rA, offA[x], sbyte(0));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kRing; ++j) {
-#pragma unroll
-                for (int f = 0; f < 2; ++f)
-                    bs[j][f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], sscale(j), 0);
-#pragma unroll
-                for (int x = 0; x < kU; ++x)
-                    as[j][x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], sscale(j + 1), 0);
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int f = 0; f < 2; ++f) bq[j][f] = load16(rB, offB[f], sbyte(j));
                 __builtin_amdgcn_sched_barrier(0);
@@ -461,9 +490,10 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
                 for (int x = 0; x < kU; ++x) aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
+            scale_store(0);
 #pragma unroll
             for (int x = 0; x < kU; ++x) {
-                const h2_t sa = scales2(as0[x], sshift);
+                const h2_t sa = scales2(scale_a(0, x), sshift);
 #pragma unroll
                 for (int v = 0; v < kKSteps; ++v) adst[x][v * kWave] = dequant8((uint32_t)a0[x][v], sa[v >> 1]);
             }
@@ -476,8 +506,8 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 
         auto stage = [&](auto parity, int i) {
             constexpr int p = decltype(parity)::value;
-            const uint32_t sb2 = sbyte(i + kRing), ss2 = sscale(i + kRing);
-            const uint32_t sb3 = sbyte(i + 1 + kRing), ss3 = sscale(i + 1 + kRing);
+            const uint32_t sb2 = sbyte(i + kRing);
+            const uint32_t sb3 = sbyte(i + 1 + kRing);
             // LDS A buffers: this stage reads buffer i % 2 and writes the other.
             const int lb = i & 1;
             const AStage& ard = sm.a[lb];
@@ -486,19 +516,17 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             for (int x = 0; x < kU; ++x)
                 awr[x] = reinterpret_cast<h8_t*>(reinterpret_cast<char*>(adst[x]) + (lb ^ 1) * abuf_step[x]);
             // Scales of this stage (B) and of the A being dequantised
-            // (stage i + 1), converted before their registers are re-loaded.
-            const h2_t sbf[2] = {scales2(bs[p][0], sshift), scales2(bs[p][1], sshift)};
+            // (stage i + 1, or this one past the chain's end), from the
+            // staging array.  Block b + 1's scales go out at the first stage
+            // of block b and are staged at its third stage, before the A of
+            // its first stage needs them.
+            const int ia = i + 1 < n ? i + 1 : i;
+            const h2_t sbf[2] = {scales2(scale_b(i, 0), sshift), scales2(scale_b(i, 1), sshift)};
             h2_t saf[2];
 #pragma unroll
-            for (int x = 0; x < kU; ++x) saf[x] = scales2(as[p][x], sshift);
-            fence_after(sbf[0]);
-            fence_after(sbf[1]);
-#pragma unroll
-            for (int x = 0; x < kU; ++x) fence_after(saf[x]);
-#pragma unroll
-            for (int f = 0; f < 2; ++f) bs[p][f] = __builtin_amdgcn_raw_buffer_load_b32(rSB, offSB[f], ss2, 0);
-#pragma unroll
-            for (int x = 0; x < kU; ++x) as[p][x] = __builtin_amdgcn_raw_buffer_load_b32(rSA, offSA[x], ss3, 0);
+            for (int x = 0; x < kU; ++x) saf[x] = scales2(scale_a(ia, x), sshift);
+            if ((i & 3) == 0 && i + 4 < n) scale_load(i + 4);
+            if ((i & 3) == 2 && i + 2 < n) scale_store(((i >> 2) + 1) & 1);
 
             // k-step pipeline: the B dequant of k-step v + 1 is issued before
             // the MFMAs of k-step v; the scheduling barrier at the end of each
