@@ -78,6 +78,9 @@ constexpr int kSlotFloats = kWaves * kMaxAFrags * 2 * kWave * 4;   // one partia
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
 constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
+// A partial-slot offset past the end of every workspace (the host checks
+// that the workspace stays below it): buffer loads there return zeros.
+constexpr uint32_t kNoSlot = 0xF0000000u;
 
 // Issue-order hints that interleave the B dequantisation with the MFMAs of
 // each k-step (0 leaves the order to the compiler).
@@ -225,24 +228,23 @@ __device__ __forceinline__ f4_t zero_acc()
     return z;
 }
 
-// The output tile of the workgroup, fp32 -> fp16 (round to nearest even,
-// overflow to inf), written to C through LDS so that every global store is
-// 16 contiguous bytes of a row.  Wave w holds B fragments 2w, 2w + 1 (16
-// columns each): acc[i][f] element r of lane (c16, kq) is tile row
-// 16 i + c16, tile column 32 w + 16 f + 4 kq + r.  Called by every thread
-// of the workgroup; the LDS is free on return.
+// Piece (i, f) of the output tile, fp32 -> fp16 (round to nearest even,
+// overflow to inf), into the LDS copy of the tile.  Wave w holds B fragments
+// 2w, 2w + 1 (16 columns each): element r of lane (c16, kq) is tile row
+// 16 i + c16, tile column 32 w + 16 f + 4 kq + r.
+__device__ __forceinline__ void stage_c(SharedMem& sm, int i, int f, const f4_t& v, int wave, int lane)
+{
+    const int c16 = lane & 15, kq = lane >> 4;
+    *reinterpret_cast<uint2*>(&sm.ctile[16 * i + c16][32 * wave + 16 * f + 4 * kq]) = pack4(v);
+}
+
+// The LDS copy of the output tile to C, every global store 16 contiguous
+// bytes of a row.  Called by every thread of the workgroup once all pieces
+// are staged; the LDS is free on return.
 template <int MF>
-__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0,
-                                        const f4_t (*acc)[2], int wave)
+__device__ __forceinline__ void write_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0)
 {
     const int tid = opaque_tid();
-    const int lane = tid % kWave;
-    const int c16 = lane & 15, kq = lane >> 4;
-#pragma unroll
-    for (int i = 0; i < 2 * MF; ++i)
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-            *reinterpret_cast<uint2*>(&sm.ctile[16 * i + c16][32 * wave + 16 * f + 4 * kq]) = pack4(acc[i][f]);
     lds_barrier();
     const int M = ga.M, N = ga.N;
     const int rows = M - m0 < MF * kFragRows ? M - m0 : MF * kFragRows;
@@ -261,6 +263,19 @@ __device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int 
         }
     }
     lds_barrier();
+}
+
+// The output tile of the workgroup from the accumulators of its waves.
+template <int MF>
+__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0,
+                                        const f4_t (*acc)[2], int wave)
+{
+    const int lane = opaque_tid() % kWave;
+#pragma unroll
+    for (int i = 0; i < 2 * MF; ++i)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) stage_c(sm, i, f, acc[i][f], wave, lane);
+    write_c<MF>(sm, ga, m0, n0);
 }
 
 // One wave's fp32 block of a partial tile (2 MF x 2 x 4 floats per lane) at
@@ -641,21 +656,73 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     __syncthreads();   // s_flag is reused by the next segment
     if (!last) return;
     // Sum the contributors' partials in workgroup order, so the result does
-    // not depend on who arrived last.  When this workgroup is the first
-    // contributor its partial is still in registers; otherwise the sum
-    // starts from zero and every partial, its own included, is read back.
-    // (A select rather than a branch, so there is one copy of the
-    // accumulators.)  The loads carry the device-scope coherence bit as well.
-    const bool keep = me == w_first;
+    // not depend on who arrived last.  Loads carry the device-scope
+    // coherence bit; a contributor index past w_last gets an offset beyond
+    // the buffer, whose loads return zeros.
+    constexpr int kPieces = 4 * MF;
+    auto load_piece = [&](int w, int q) {
+        const uint32_t base = w <= w_last ? slot_base(w) : kNoSlot;
+        return __builtin_bit_cast(
+            f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
+    };
+    if (me == w_first) {
+        // This workgroup's partial is still in the accumulators (often the
+        // case: the first contributor ends its range with the tile's first
+        // stages, so it tends to finish last); the others are added to it,
+        // kChunk pieces of kBatch contributors in flight.  Tiles of 4 or more
+        // fragments take one contributor at a time (in two halves for 6
+        // fragments): their accumulators hold the registers.
+        constexpr int kChunk = MF <= 5 ? kPieces : kPieces / 2;
+        constexpr int kBatch = MF <= 3 ? 24 / kChunk : 1;
+        for (int w0 = w_first + 1; w0 <= w_last; w0 += kBatch) {
 #pragma unroll
-    for (int a = 0; a < 2 * MF; ++a)
+            for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+                f4_t v[kBatch][kChunk];
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+                for (int b = 0; b < kBatch; ++b)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[a][f][e] = keep ? acc[a][f][e] : 0.0f;
-    for (int w = keep ? w_first + 1 : w_first; w <= w_last; ++w) load_block<MF>(rP, slot_base(w), acc);
-    asm volatile("; fix-up" ::: "memory");
-    store_c<MF>(sm, ga, m0, n0, acc, wave);
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                        acc[(q0 + q) >> 1][(q0 + q) & 1] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("; fix-up, first contributor" ::: "memory");
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
+    } else {
+        // Every partial, this workgroup's own included, is read back, so the
+        // accumulators are free: kChunk pieces of kBatch contributors in
+        // flight, each summed chunk straight to the LDS copy of the tile.
+        constexpr int kChunk = MF <= 3 ? kPieces : kPieces / 2;
+        constexpr int kBatch = (MF <= 2 ? 32 : 24) / kChunk;
+        const int flane = opaque_tid() % kWave;
+#pragma unroll
+        for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+            f4_t sum[kChunk];
+#pragma unroll
+            for (int q = 0; q < kChunk; ++q) sum[q] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int w0 = w_first; w0 <= w_last; w0 += kBatch) {
+                f4_t v[kBatch][kChunk];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) sum[q] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                stage_c(sm, (q0 + q) >> 1, (q0 + q) & 1, sum[q], wave, flane);
+        }
+        asm volatile("; fix-up" ::: "memory");
+        write_c<MF>(sm, ga, m0, n0);
+    }
     if (threadIdx.x == 0)
         __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -890,30 +957,42 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
     int gi = 0;
     while (gi < g) {
         std::memset(&args, 0, sizeof(args));
+        // The next (up to) kMaxGroups non-empty groups form one launch.
+        int idx[kMaxGroups], bM[kMaxGroups], bN[kMaxGroups], bK[kMaxGroups];
         int n = 0;
-        int tiles = 0;
-        int64_t cost = 0;
         for (; gi < g && n < kMaxGroups; ++gi) {
             if (M[gi] == 0 || N[gi] == 0 || K[gi] == 0) continue;
-            GroupSched& sc = args.sched[n];
-            GroupArgs& ga = args.grp[n];
+            idx[n] = gi;
+            bM[n] = M[gi];
+            bN[n] = N[gi];
+            bK[n] = K[gi];
             ++n;
-            ga.A = static_cast<const uint8_t*>(A_ptrs[gi]);
-            ga.B = static_cast<const uint8_t*>(B_ptrs[gi]);
-            ga.SFA = static_cast<const uint8_t*>(SFA_ptrs[gi]);
-            ga.SFB = static_cast<const uint8_t*>(SFB_ptrs[gi]);
-            ga.C = static_cast<uint16_t*>(C_ptrs[gi]);
-            ga.M = M[gi];
-            ga.N = N[gi];
-            ga.K = K[gi];
-            sc = make_group_sched(M[gi], N[gi], K[gi], cost, tiles);
+        }
+        if (n == 0) continue;
+        const int maxf = choose_max_frags(n, bM, bN, bK, cus);
+        int tiles = 0;
+        int64_t cost = 0;
+        for (int j = 0; j < n; ++j) {
+            const int q = idx[j];
+            GroupSched& sc = args.sched[j];
+            GroupArgs& ga = args.grp[j];
+            ga.A = static_cast<const uint8_t*>(A_ptrs[q]);
+            ga.B = static_cast<const uint8_t*>(B_ptrs[q]);
+            ga.SFA = static_cast<const uint8_t*>(SFA_ptrs[q]);
+            ga.SFB = static_cast<const uint8_t*>(SFB_ptrs[q]);
+            ga.C = static_cast<uint16_t*>(C_ptrs[q]);
+            ga.M = M[q];
+            ga.N = N[q];
+            ga.K = K[q];
+            sc = make_group_sched(M[q], N[q], K[q], cost, tiles, maxf);
             cost += group_cost(sc);
             tiles += sc.mblocks * sc.nblocks;
         }
-        if (n == 0) continue;
         args.ngroups = n;
         args.W = cost;
         args.G = grid_size(cost, cus);
+        if ((uint64_t)kSlotsPerWG * args.G * kSlotFloats * 4u >= kNoSlot)
+            return fail(NVFP4GG_UNSUPPORTED, "too many compute units for the partial-tile workspace");
         Workspace ws;
         const int rc = get_workspace(dev, s, args.G, tiles, ws);
         if (rc != NVFP4GG_OK) return rc;

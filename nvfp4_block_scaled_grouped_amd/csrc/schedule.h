@@ -6,10 +6,11 @@
 //
 // Terms:
 //   * fragment: 32 rows of A_i (the MFMA tile height).
-//   * m-block: up to kMaxFrags fragments of one group, processed together.
-//     A group with F = ceil(M/32) fragments has nmb = ceil(F / kMaxFrags)
-//     m-blocks; fragments are spread evenly, so the first F % nmb m-blocks
-//     get F / nmb + 1 fragments and the rest F / nmb.
+//   * m-block: up to maxf <= kMaxFrags fragments of one group, processed
+//     together (maxf is chosen per launch).  A group with F = ceil(M/32)
+//     fragments has nmb = ceil(F / maxf) m-blocks; fragments are spread
+//     evenly, so the first F % nmb m-blocks get F / nmb + 1 fragments and
+//     the rest F / nmb.
 //   * n-block: kTileN columns of B_i.
 //   * tile: (group, n-block, m-block); tiles are ordered by group, then
 //     n-block, then m-block, so the m-blocks that share a B strip are
@@ -43,7 +44,7 @@ constexpr int kTileN = 256;        // columns per n-block
 constexpr int kStageK = 128;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
 constexpr int kTileCost = 200;     // cost units of a tile beyond its stages
-constexpr int kMaxUnitCost = 53;   // the costliest stage (6 fragments)
+constexpr int kMaxUnitCost = 56;   // the costliest stage (6 fragments)
 // Least cost handed to one workgroup: keeps every workgroup range longer
 // than the costliest stage, so the workgroups sharing a tile are
 // consecutive.
@@ -62,25 +63,25 @@ struct GroupSched {
 NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
 // The schedule entry of a group with M, N >= 1 and K a positive multiple of
-// kStageK.
-NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin)
+// kStageK, in m-blocks of at most maxf (1..kMaxFrags) fragments.
+NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin, int maxf = kMaxFrags)
 {
     GroupSched g;
     g.cost_begin = cost_begin;
     g.tile_begin = tile_begin;
     g.frags = ceil_div_i(M, kFragRows);
-    g.mblocks = ceil_div_i(g.frags, kMaxFrags);
+    g.mblocks = ceil_div_i(g.frags, maxf);
     g.nblocks = ceil_div_i(N, kTileN);
     g.stages = K / kStageK;
     return g;
 }
 
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
-// about 50 ns (measured MI355X stage times: 1.5, 1.6, 1.8, 2.3 and 2.7 us for
-// 2 to 6 fragments; one fragment extrapolated).
+// about 50 ns (measured MI355X stage times: 1.2, 1.45, 1.75, 2.3 and 2.8 us
+// for 2 to 6 fragments; one fragment extrapolated).
 NVFP4_HD int unit_cost(int f)
 {
-    return f <= 1 ? 28 : f == 2 ? 30 : f == 3 ? 32 : f == 4 ? 35 : f == 5 ? 47 : kMaxUnitCost;
+    return f <= 1 ? 21 : f == 2 ? 24 : f == 3 ? 29 : f == 4 ? 35 : f == 5 ? 46 : kMaxUnitCost;
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
@@ -173,6 +174,45 @@ NVFP4_HD int grid_size(int64_t W, int cus)
     if (G > kXcds) G -= G % kXcds;
     if (G < 1) G = 1;
     return (int)G;
+}
+
+// Cost of splitting a tile once more (about 3.9 us, measured): one more
+// partial tile stored by a contributor and read back by the fix-up.
+constexpr int kSplitCost = 78;
+
+// Estimated time of a launch of total cost W over G workgroups holding
+// `tiles` tiles, in cost units: one workgroup's range, plus kSplitCost for
+// each contributor beyond the first of an average tile.
+inline double launch_estimate(int64_t W, int G, int tiles)
+{
+    const double extra = (double)G / tiles - 1.0;
+    return (double)W / G + (extra > 0.0 ? kSplitCost * extra : 0.0);
+}
+
+// The m-block size (1..kMaxFrags fragments) of a launch of n non-empty
+// groups on cus CUs with the least launch_estimate, the largest on ties.
+// Large m-blocks stream each B strip once and run the MFMAs densest; smaller
+// ones give problems with few tiles more of them, so fewer workgroups share
+// a tile.
+inline int choose_max_frags(int n, const int* M, const int* N, const int* K, int cus)
+{
+    int best = kMaxFrags;
+    double best_t = 0.0;
+    for (int maxf = kMaxFrags; maxf >= 1; --maxf) {
+        int64_t W = 0;
+        int tiles = 0;
+        for (int i = 0; i < n; ++i) {
+            const GroupSched g = make_group_sched(M[i], N[i], K[i], W, tiles, maxf);
+            W += group_cost(g);
+            tiles += g.mblocks * g.nblocks;
+        }
+        const double t = launch_estimate(W, grid_size(W, cus), tiles);
+        if (maxf == kMaxFrags || t < best_t) {
+            best = maxf;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 // Workgroup boundary b_w = floor(w * W / G) (w = 0..G).

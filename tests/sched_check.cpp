@@ -15,25 +15,30 @@ using namespace nvfp4sched;
 static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { ++fails; std::printf("FAIL %s:%d: ", __FILE__, __LINE__); std::printf(__VA_ARGS__); std::printf("\n"); return; } } while (0)
 
-static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus)
+static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus, int maxf)
 {
     int ng = (int)M.size();
+    CHECK(maxf >= 1 && maxf <= kMaxFrags, "m-block size %d", maxf);
     GroupSched gs[kMaxGroups];
     int64_t cost = 0;
     int tiles = 0;
     for (int i = 0; i < ng; ++i) {
-        gs[i] = make_group_sched(M[i], N[i], K[i], cost, tiles);
+        gs[i] = make_group_sched(M[i], N[i], K[i], cost, tiles, maxf);
         cost += group_cost(gs[i]);
         tiles += gs[i].mblocks * gs[i].nblocks;
-        // m-block partition covers all fragments, each block 1..kMaxFrags
+        // m-block partition covers all fragments, each block 1..maxf, sizes
+        // differing by at most one
         int sum = 0;
         for (int b = 0; b < gs[i].mblocks; ++b) {
             int f = mblock_frags(gs[i].frags, gs[i].mblocks, b);
-            CHECK(f >= 1 && f <= kMaxFrags, "mblock frags %d", f);
+            CHECK(f >= 1 && f <= maxf, "mblock frags %d", f);
+            CHECK(f >= mblock_frags(gs[i].frags, gs[i].mblocks, gs[i].mblocks - 1), "uneven m-blocks");
+            CHECK(f <= mblock_frags(gs[i].frags, gs[i].mblocks, gs[i].mblocks - 1) + 1, "uneven m-blocks");
             CHECK(mblock_first_frag(gs[i].frags, gs[i].mblocks, b) == sum, "first frag");
             sum += f;
         }
         CHECK(sum == gs[i].frags, "frag sum");
+        CHECK(gs[i].mblocks == (gs[i].frags + maxf - 1) / maxf, "m-block count");
         // the closed-form m-block cost prefix matches the sum of its tiles
         int64_t c = 0;
         for (int b = 0; b <= gs[i].mblocks; ++b) {
@@ -100,15 +105,28 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
     }
 }
 
+// The launch's m-block size as the host picks it, then the schedule check.
+static void run_launch(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus)
+{
+    const int maxf = choose_max_frags((int)M.size(), M.data(), N.data(), K.data(), cus);
+    run_case(M, N, K, cus, maxf);
+}
+
 int main()
 {
-    // The five workloads.
-    run_case({64, 96}, {256, 256}, {512, 512}, 256);
-    run_case({128, 384}, {4096, 4096}, {1536, 1536}, 256);
-    run_case({192, 320}, {3072, 3072}, {4096, 4096}, 256);
-    run_case({40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048), 256);
-    run_case({80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168), 256);
-    // Random shapes and grid sizes.
+    // The five workloads, at the size the host picks and at every size.
+    const std::vector<std::vector<std::vector<int>>> five = {
+        {{64, 96}, {256, 256}, {512, 512}},
+        {{128, 384}, {4096, 4096}, {1536, 1536}},
+        {{192, 320}, {3072, 3072}, {4096, 4096}},
+        {{40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048)},
+        {{80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168)},
+    };
+    for (const auto& w : five) {
+        run_launch(w[0], w[1], w[2], 256);
+        for (int maxf = 1; maxf <= kMaxFrags; ++maxf) run_case(w[0], w[1], w[2], 256, maxf);
+    }
+    // Random shapes, grid sizes and m-block sizes.
     std::mt19937 rng(12345);
     for (int it = 0; it < 3000; ++it) {
         const int ng = 1 + rng() % 12;
@@ -118,7 +136,11 @@ int main()
             N.push_back(1 + rng() % 3000);
             K.push_back(kStageK * (1 + rng() % 24));
         }
-        run_case(M, N, K, 1 + rng() % 300);
+        const int cus = 1 + rng() % 300;
+        if (it % 2 == 0)
+            run_launch(M, N, K, cus);
+        else
+            run_case(M, N, K, cus, 1 + rng() % kMaxFrags);
         if (fails) break;
     }
     if (fails) { std::printf("FAILED %d\n", fails); return 1; }
