@@ -79,6 +79,26 @@ int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
                      const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                      void* const* C_ptrs, void* stream);
 
+/* The same grouped GEMM with SFA_i and SFB_i in the blocked scale layout
+ * that the pages' kernels consume (page 482006: to_blocked_gpu in its cuBLAS
+ * path, and the scale-factor layout atom of its CuTe kernel, shape
+ * ((32,4),(16,4)) with strides ((16,4),(0,1)); page 505431, the scale-factor
+ * copy comment block of its kernel).  A scale array of R rows and S = K_i/16
+ * scale columns is padded to R' = ceil(R/128)*128 rows and S' = ceil(S/4)*4
+ * columns and cut into 128 x 4 atoms of 512 bytes, atoms of one 128-row band
+ * consecutive in column order, bands in row order.  Inside an atom, row r
+ * (0..127) and column c (0..3) are byte 16*(r%32) + 4*(r/32) + c.  So the
+ * scale of row r, column s is byte
+ *     512*((r/128)*(S'/4) + s/4) + 16*(r%32) + 4*((r/32)%4) + s%4.
+ * SFA_i holds ceil(M_i/128)*128*K_i/16 bytes, SFB_i ceil(N_i/128)*128*K_i/16
+ * (K_i % 128 == 0 is required anyway, so S' = S).  Padding bytes are never
+ * used in a result.  All other arguments, layouts, ownership, workspace and
+ * return codes as nvfp4_group_gemm. */
+int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,
+                             const void* const* A_ptrs, const void* const* B_ptrs,
+                             const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                             void* const* C_ptrs, void* stream);
+
 /* The dequantisation step alone, with the same device code the GEMM uses:
  * out[r][k] = fp16( e2m1(X[r][k]) * e4m3(SFX[r][k/16]) ) for a rows x K
  * packed FP4 matrix X and its rows x K/16 scales (layouts as A_i, SFA_i
@@ -92,7 +112,7 @@ int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (2 added nvfp4_group_gemm_blocked). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

@@ -116,6 +116,7 @@ struct LaunchArgs {
     int64_t W;            // total cost
     int G;                // workgroups
     int ngroups;
+    int blocked_sf;       // scales in the blocked (128 x 4 atom) layout, else row-major
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
@@ -398,8 +399,13 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
+    // Blocked scales: rows padded to a multiple of 128 (the layout's atoms
+    // are 128 rows x 4 scales; K / 16 is a multiple of 8 here).
+    const bool blocked = args.blocked_sf != 0;
+    const uint32_t sf_rows_a = blocked ? (uint32_t)(M + 127) & ~127u : (uint32_t)M;
+    const uint32_t sf_rows_b = blocked ? (uint32_t)(N + 127) & ~127u : (uint32_t)N;
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, sf_rows_a * row_scales);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, sf_rows_b * row_scales);
     const uint32_t sshift = 16u * (uint32_t)(kq & 1);   // this lane's scale bytes within a dword
 
     // B operand of lane (c16, kq) in fragment f: row n0 + 32 wave + 16 f + c16
@@ -453,23 +459,47 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         // itself reads its rows, and a wave's LDS accesses complete in issue
         // order, so no barrier guards them.  A block that runs past the end
         // of K reads the next row's bytes or, past the buffer, zeros; the
-        // stages that use them do not exist.
+        // stages that would use them do not exist.
+        //
+        // Row-major scales: the 16 bytes are contiguous.  Blocked scales
+        // (the 128 x 4 atom layout): scale column c of row r is byte
+        // 512 ((r / 128) (K / 64) + c / 4) + 16 (r % 32) + 4 ((r / 32) % 4)
+        // + c % 4, so the 16 bytes are four 4-byte runs (scale columns
+        // 4q .. 4q + 3 of consecutive atoms), 512 bytes apart.
         const int slane = lane;
-        const uint32_t offSBs = (uint32_t)(n0 + 32 * wave + (slane >> 1)) * row_scales + 16u * (slane & 1);
+        auto sf_off = [&](int r) {
+            return blocked ? (uint32_t)(r >> 7) * (uint32_t)K * 8u + (uint32_t)(r & 31) * 16u +
+                                 (uint32_t)((r >> 5) & 3) * 4u + 2048u * (slane & 1)
+                           : (uint32_t)r * row_scales + 16u * (slane & 1);
+        };
+        const uint32_t offSBs = sf_off(n0 + 32 * wave + (slane >> 1));
         uint32_t offSAs[2];
 #pragma unroll
         for (int x = 0; x < kU; ++x) {
             const int a = wave + kWaves * x;
-            offSAs[x] = (uint32_t)(m0 + 16 * (a % NA) + ((slane >> 1) & 15)) * row_scales + 16u * (slane & 1);
+            offSAs[x] = sf_off(m0 + 16 * (a % NA) + ((slane >> 1) & 15));
         }
-        auto sblock = [&](int b) {   // scale byte offset of the block starting at stage b of the chain
-            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (kStageK / 16));
+        // Offset of the block starting at stage b of the chain: 8 scale
+        // bytes per stage, in row-major scales one atom (512 bytes) per 4
+        // scale columns in blocked ones.
+        auto sblock = [&](int b) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (blocked ? 1024 : kStageK / 16));
         };
+        auto sload = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+            if (!blocked) return load16(r, voff, soff);
+            i4_t v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 512u * j, soff, 0);
+            return v;
+        };
+        // The block offset goes into the per-lane offset, which the buffer's
+        // range check covers (the scalar offset is not checked): a block
+        // that runs past the end of the last row reads zeros there.
         i4_t sregB, sregA[2];
         auto scale_load = [&](int b) {
-            sregB = load16(rSB, offSBs, sblock(b));
+            sregB = sload(rSB, offSBs + sblock(b), 0);
 #pragma unroll
-            for (int x = 0; x < kU; ++x) sregA[x] = load16(rSA, offSAs[x], sblock(b));
+            for (int x = 0; x < kU; ++x) sregA[x] = sload(rSA, offSAs[x] + sblock(b), 0);
         };
         auto scale_store = [&](int buf) {
             *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][slane >> 1][4 * (slane & 1)]) = sregB;
@@ -898,12 +928,14 @@ int device_cus(int dev)
 
 extern "C" const char* nvfp4_group_gemm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int nvfp4_group_gemm_version(void) { return 1; }
+extern "C" int nvfp4_group_gemm_version(void) { return 2; }
 
-extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
-                                const void* const* A_ptrs, const void* const* B_ptrs,
-                                const void* const* SFA_ptrs, const void* const* SFB_ptrs,
-                                void* const* C_ptrs, void* stream)
+namespace {
+
+// Both entry points: blocked_sf selects the layout of the scale arrays.
+int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void* const* A_ptrs,
+                    const void* const* B_ptrs, const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                    void* const* C_ptrs, void* stream, int blocked_sf)
 {
     g_last_error.clear();
     if (g <= 0) return fail(NVFP4GG_INVALID_ARG, "g must be >= 1");
@@ -989,6 +1021,7 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
             tiles += sc.mblocks * sc.nblocks;
         }
         args.ngroups = n;
+        args.blocked_sf = blocked_sf;
         args.W = cost;
         args.G = grid_size(cost, cus);
         if ((uint64_t)kSlotsPerWG * args.G * kSlotFloats * 4u >= kNoSlot)
@@ -1004,6 +1037,24 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
             return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
     }
     return NVFP4GG_OK;
+}
+
+}  // namespace
+
+extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
+                                const void* const* A_ptrs, const void* const* B_ptrs,
+                                const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                                void* const* C_ptrs, void* stream)
+{
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0);
+}
+
+extern "C" int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,
+                                        const void* const* A_ptrs, const void* const* B_ptrs,
+                                        const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                                        void* const* C_ptrs, void* stream)
+{
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 1);
 }
 
 extern "C" int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX, void* out, void* stream)

@@ -94,6 +94,41 @@ def round_f16_double(x: float) -> int:
     return int(_load().oracle_round_f16_double(float(x)))
 
 
+def blocked_scale_bytes(rows: int, cols: int) -> int:
+    """Size of the blocked layout of a rows x cols scale matrix."""
+    lib = _load()
+    lib.oracle_blocked_scale_bytes.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.oracle_blocked_scale_bytes.restype = ctypes.c_int64
+    return int(lib.oracle_blocked_scale_bytes(int(rows), int(cols)))
+
+
+def block_scales(plain: np.ndarray, rows: int, cols: int, pad_value: int = 0) -> np.ndarray:
+    """The blocked layout (flat uint8) of a row-major rows x cols scale matrix;
+    pad bytes are pad_value."""
+    plain = np.ascontiguousarray(plain, dtype=np.uint8)
+    assert plain.size == rows * cols
+    out = np.empty(blocked_scale_bytes(rows, cols), dtype=np.uint8)
+    lib = _load()
+    lib.oracle_block_scales.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint8),
+                                        ctypes.POINTER(ctypes.c_uint8), ctypes.c_uint8]
+    if lib.oracle_block_scales(int(rows), int(cols), _u8ptr(plain), _u8ptr(out), int(pad_value)) != 0:
+        raise ValueError("oracle_block_scales: bad sizes")
+    return out
+
+
+def unblock_scales(blocked: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """The row-major rows x cols scale matrix held in a blocked array."""
+    blocked = np.ascontiguousarray(blocked, dtype=np.uint8)
+    assert blocked.size >= blocked_scale_bytes(rows, cols)
+    out = np.empty((rows, cols), dtype=np.uint8)
+    lib = _load()
+    lib.oracle_unblock_scales.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint8),
+                                          ctypes.POINTER(ctypes.c_uint8)]
+    if lib.oracle_unblock_scales(int(rows), int(cols), _u8ptr(blocked), _u8ptr(out)) != 0:
+        raise ValueError("oracle_unblock_scales: bad sizes")
+    return out
+
+
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
 

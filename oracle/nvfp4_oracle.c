@@ -254,6 +254,56 @@ int oracle_dequant(int rows, int K, const uint8_t* X, const uint8_t* SFX, double
     return 0;
 }
 
+/* ------------------------------------------------------ blocked scale layout
+ *
+ * The layout the pages' kernels read their scales in (page 482006, function
+ * to_blocked_gpu of its cuBLAS path, and the scale-factor layout atom of its
+ * CuTe kernel; page 505431, the scale-factor copy comment block).  Taken in
+ * the order those passages describe it:
+ *   1. the rows x cols scale matrix is padded with zeros to a multiple of 128
+ *      rows and of 4 columns;
+ *   2. it is cut into blocks of 128 rows x 4 columns; the blocks of one
+ *      128-row band follow each other in column order, the bands in row
+ *      order, 512 bytes per block;
+ *   3. inside a block the 128 rows form 4 groups of 32; the block is 32 runs
+ *      of 16 bytes, run j holding, in turn, the 4 columns of rows j, j + 32,
+ *      j + 64 and j + 96.
+ * oracle_block_scales writes a blocked array (pad bytes = pad_value) from a
+ * row-major one; oracle_unblock_scales reads the row-major matrix back. */
+static int64_t blocked_pos(int64_t r, int64_t c, int64_t band_blocks)
+{
+    const int64_t band = r / 128, rb = r % 128;   /* step 2: which band, row in band */
+    const int64_t block = band * band_blocks + c / 4;
+    const int64_t run = rb % 32, group = rb / 32;  /* step 3 */
+    return block * 512 + run * 16 + group * 4 + c % 4;
+}
+
+int64_t oracle_blocked_scale_bytes(int rows, int cols)
+{
+    if (rows < 0 || cols < 0) return -1;
+    return ((int64_t)(rows + 127) / 128) * 128 * (((int64_t)cols + 3) / 4 * 4);
+}
+
+int oracle_block_scales(int rows, int cols, const uint8_t* plain, uint8_t* blocked, uint8_t pad_value)
+{
+    const int64_t n = oracle_blocked_scale_bytes(rows, cols);
+    if (n < 0) return -1;
+    memset(blocked, pad_value, (size_t)n);
+    const int64_t band_blocks = ((int64_t)cols + 3) / 4;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) blocked[blocked_pos(r, c, band_blocks)] = plain[r * cols + c];
+    return 0;
+}
+
+int oracle_unblock_scales(int rows, int cols, const uint8_t* blocked, uint8_t* plain)
+{
+    if (rows < 0 || cols < 0) return -1;
+    const int64_t band_blocks = ((int64_t)cols + 3) / 4;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) plain[r * cols + c] = blocked[blocked_pos(r, c, band_blocks)];
+    return 0;
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert nv.version() == 1
+    assert nv.version() == 2
 
 
 A16 = 0x10000          # fake, aligned addresses: never dereferenced, every case
@@ -113,3 +113,17 @@ def test_binding_rejects_host_tensors(lib):
     c = torch.zeros(16, dtype=torch.float16)
     with pytest.raises(ValueError):
         nv.group_gemm([t], [t], [t[:16]], [t[:16]], [c.view(4, 4)], M=[4], N=[4], K=[64])
+
+
+def test_blocked_entry_validates_like_the_plain_one(lib):
+    assert lib.nvfp4_group_gemm_blocked(0, None, None, None, None, None, None, None, None, None) == nv.INVALID_ARG
+    rc = nv.group_gemm_ptrs([8], [8], [144], [A16], [A16], [A16], [A16], [A16], 0, blocked=True)
+    assert rc == nv.UNSUPPORTED and "K % 128" in nv.last_error()
+    rc = nv.group_gemm_ptrs([8], [8], [256], [MIS], [A16], [A16], [A16], [A16], 0, blocked=True)
+    assert rc == nv.INVALID_ARG
+
+
+def test_blocked_scale_bytes():
+    assert nv.blocked_scale_bytes(1, 128) == 128 * 8
+    assert nv.blocked_scale_bytes(128, 7168) == 128 * 448
+    assert nv.blocked_scale_bytes(129, 256) == 256 * 16

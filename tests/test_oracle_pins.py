@@ -6,6 +6,7 @@ the oracle's own code: see tests/_independent.py for the sources used.
 from __future__ import annotations
 
 import math
+import os
 
 import numpy as np
 import pytest
@@ -273,3 +274,64 @@ def test_pins_detect_plausible_mistakes(oracle_lib):
     assert not np.array_equal(ind.brute_group(A, B, SA32, SB, M, N, K)[1], base)
     C = oracle_lib.group_gemm([M], [N], [K], [A], [B], [SA], [SB])[0]
     np.testing.assert_array_equal(C.view(np.uint16), base16.view(np.uint16))
+
+
+# ------------------------------------------------------ blocked scale layout
+
+def _cute_atom_offsets(rows, cols):
+    """Byte offset of every (row, scale column) of a rows x cols scale matrix,
+    evaluated from the layout algebra printed with page 482006's CuTe kernel:
+    the atom has shape ((32, 4), (16, 4)) and strides ((16, 4), (0, 1)) over
+    (row, K), so a row r = r0 + 32 r1 contributes 16 r0 + 4 r1 and a K index
+    k = k0 + 16 k1 (k0 < 16 shares one scale) contributes k1; atoms are tiled
+    over (M, K) with the K tiles first (tile order (2, 1, 3)), 512 bytes each.
+    Independent of the oracle's row-band/run formulation."""
+    ktiles = -(-cols // 4)
+    r = np.arange(rows)[:, None]
+    s = np.arange(cols)[None, :]
+    k = 16 * s                                    # first K index of scale column s
+    r0, r1, tm = r % 32, (r // 32) % 4, r // 128
+    k1, tk = (k // 16) % 4, k // 64
+    return 16 * r0 + 4 * r1 + 0 * (k % 16) + k1 + 512 * (tk + ktiles * tm)
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 4), (128, 4), (130, 8), (300, 12), (64, 448)])
+def test_blocked_layout_matches_cute_atom(oracle_lib, rows, cols):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    plain = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+    blocked = oracle_lib.block_scales(plain, rows, cols, pad_value=0)
+    assert blocked.size == (-(-rows // 128) * 128) * (-(-cols // 4) * 4)
+    off = _cute_atom_offsets(rows, cols)
+    np.testing.assert_array_equal(blocked[off], plain)
+    # the layout is a bijection: every byte of the padded matrix has its own place
+    assert len(np.unique(off)) == rows * cols
+    np.testing.assert_array_equal(oracle_lib.unblock_scales(blocked, rows, cols), plain)
+
+
+def test_blocked_layout_golden(oracle_lib):
+    """Hand-placed positions (tests/golden/blocked_scales_130x8.txt) of a
+    130 x 8 scale matrix whose byte at (r, c) is a distinct tag."""
+    rows, cols = 130, 8
+    plain = ((np.arange(rows)[:, None] * 7 + np.arange(cols)[None, :] * 3) % 251).astype(np.uint8)
+    blocked = oracle_lib.block_scales(plain, rows, cols, pad_value=255)
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "blocked_scales_130x8.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        r, c, pos = (int(v) for v in line.split())
+        assert blocked[pos] == plain[r, c], (r, c, pos)
+    # rows 130..255 of the second band are padding
+    assert np.count_nonzero(blocked == 255) >= (256 - 130) * cols
+
+
+def test_blocked_pins_detect_plausible_mistakes(oracle_lib):
+    """A layout with the 32-row groups and the runs swapped, or with the atoms
+    of a band laid out row-first, fails the CuTe-atom pin."""
+    rows, cols = 256, 8
+    off = _cute_atom_offsets(rows, cols)
+    r = np.arange(rows)[:, None]
+    s = np.arange(cols)[None, :]
+    swapped = 512 * ((r // 128) * 2 + s // 4) + 4 * (r % 32) + 16 * ((r // 32) % 4) + s % 4
+    row_first = 512 * ((s // 4) * 2 + r // 128) + 16 * (r % 32) + 4 * ((r // 32) % 4) + s % 4
+    assert not np.array_equal(swapped, off)
+    assert not np.array_equal(row_first, off)
