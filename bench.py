@@ -57,6 +57,9 @@ def parse():
                     help="workload name (default: the g=8 K=7168 N=4096 grouped GEMM)")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through (0: enough to exceed 384 MB, at most 64)")
+    ap.add_argument("--sf-layout", choices=("row-major", "blocked"), default="row-major",
+                    help="scale layout: row-major (nvfp4_group_gemm) or the blocked 128 x 4 atom "
+                         "layout (nvfp4_group_gemm_blocked)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -126,10 +129,19 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mb: int):
     return out
 
 
-def make_device_sets(cfg, nsets, torch):
+def make_device_sets(cfg, nsets, torch, blocked=False, blocked_bytes=None):
+    """Device copies of nsets input sets.  With blocked scales, each scale
+    array is a fresh draw of scale codes of the blocked array's size (the
+    timing does not depend on which valid scale sits where)."""
     sets = []
     for v in range(nsets):
         A, B, SA, SB = workloads.config_inputs(cfg, variant=v)
+        if blocked:
+            kk = cfg["K"]
+            SA = [workloads.scale_codes(workloads.stream_key(cfg["seed"], v, i, 101), blocked_bytes(m, k))
+                  for i, (m, k) in enumerate(zip(cfg["M"], kk))]
+            SB = [workloads.scale_codes(workloads.stream_key(cfg["seed"], v, i, 102), blocked_bytes(n, k))
+                  for i, (n, k) in enumerate(zip(cfg["N"], kk))]
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         sets.append(dict(A=[dev(a) for a in A], B=[dev(b) for b in B],
                          SA=[dev(s) for s in SA], SB=[dev(s) for s in SB],
@@ -198,12 +210,13 @@ def main():
     abytes = workloads.algorithmic_bytes(M, N, K)
     flops = workloads.algorithmic_flops(M, N, K)
     nsets = args.sets or min(64, max(1, -(-384 * 2 ** 20 // abytes)))
-    sets = make_device_sets(cfg, nsets, torch)
+    blocked = args.sf_layout == "blocked"
+    sets = make_device_sets(cfg, nsets, torch, blocked, nv.blocked_scale_bytes)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     calls = [nv.GroupGemmCall(M, N, K, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
                               [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
-                              [t.data_ptr() for t in s["C"]], sh) for s in sets]
+                              [t.data_ptr() for t in s["C"]], sh, blocked=blocked) for s in sets]
 
     def step(i):
         rc = calls[i % nsets]()
@@ -236,7 +249,7 @@ def main():
 
     gbps = abytes / us / 1e3
     tflops = flops / us / 1e6
-    traffic = read_traffic(cfg["name"])
+    traffic = read_traffic(cfg["name"] + ("_blocked_sf" if blocked else ""))
     out = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -251,7 +264,7 @@ def main():
         "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "g": len(M), "M": M, "N": N[0], "K": K[0],
-                   "input_sets_rotated": nsets},
+                   "sf_layout": args.sf_layout, "input_sets_rotated": nsets},
         "us_per_call": {"mean": round(us, 3), "std": round(float(per.std()), 3),
                         "min": round(float(per.min()), 3), "max": round(float(per.max()), 3),
                         "wall_mean": round(wall / args.steps * 1e6, 3)},
