@@ -99,6 +99,24 @@ int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,
                              const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                              void* const* C_ptrs, void* stream);
 
+/* The MXFP4 form of the grouped GEMM: the same E2M1 operands A_i, B_i and
+ * fp16 output, with one E8M0 scale per 32 consecutive K of a row instead of
+ * an E4M3 scale per 16:
+ *   C_i[m][n] = sum_k a_i(m,k) * 2^(sfa_i(m, k/32) - 127) * b_i(n,k) * 2^(sfb_i(n, k/32) - 127)
+ * rounded to fp16, accumulated in fp32.  The pages name this MX block
+ * scaling beside the NVFP4 one (page 505431: the block-scaled MMA kind that
+ * covers both and the scale-type field of its instruction descriptor; page
+ * 444497, header comment) without defining it; E8M0 is read as in the OCP
+ * MX format: an unsigned 8-bit exponent, value 2^(code - 127), code 0xFF NaN.
+ *   SFA_i  M_i x K_i/32 E8M0 bytes, row-major, unpadded; SFB_i N_i x K_i/32.
+ * It runs on gfx950's block-scaled FP4 MFMA directly, with no
+ * dequantisation.  Arguments, ownership, workspace and return codes as
+ * nvfp4_group_gemm (K_i % 128 == 0 likewise). */
+int mxfp4_group_gemm(int g, const int* M, const int* N, const int* K,
+                     const void* const* A_ptrs, const void* const* B_ptrs,
+                     const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                     void* const* C_ptrs, void* stream);
+
 /* The dequantisation step alone, with the same device code the GEMM uses:
  * out[r][k] = fp16( e2m1(X[r][k]) * e4m3(SFX[r][k/16]) ) for a rows x K
  * packed FP4 matrix X and its rows x K/16 scales (layouts as A_i, SFA_i
@@ -112,7 +130,8 @@ int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 2 (2 added nvfp4_group_gemm_blocked). */
+/* ABI version of this header: 3 (2 added nvfp4_group_gemm_blocked, 3
+ * mxfp4_group_gemm). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

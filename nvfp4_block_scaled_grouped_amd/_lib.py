@@ -33,7 +33,7 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     ip = ctypes.POINTER(ctypes.c_int)
     pp = ctypes.POINTER(ctypes.c_void_p)
-    for fn in (lib.nvfp4_group_gemm, lib.nvfp4_group_gemm_blocked):
+    for fn in (lib.nvfp4_group_gemm, lib.nvfp4_group_gemm_blocked, lib.mxfp4_group_gemm):
         fn.argtypes = [ctypes.c_int, ip, ip, ip, pp, pp, pp, pp, pp, ctypes.c_void_p]
         fn.restype = ctypes.c_int
     lib.nvfp4_dequant_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -80,14 +80,25 @@ def _ptr(t, name, dtype_names):
 _BYTES = ("uint8", "int8", "float4_e2m1fn_x2", "float8_e4m3fn")
 
 
-def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False) -> int:
+def _entry(lib, blocked, fmt):
+    if fmt == "mxfp4":
+        if blocked:
+            raise ValueError("the MXFP4 entry point takes row-major scales only")
+        return lib.mxfp4_group_gemm
+    if fmt != "nvfp4":
+        raise ValueError("fmt must be 'nvfp4' or 'mxfp4'")
+    return lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
+
+
+def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False, fmt="nvfp4") -> int:
     """Raw call: sizes are Python ints, operands are integer device addresses.
-    blocked selects nvfp4_group_gemm_blocked (scales in the blocked layout).
-    Returns the library's status code without raising."""
+    blocked selects nvfp4_group_gemm_blocked (scales in the blocked layout),
+    fmt="mxfp4" mxfp4_group_gemm.  Returns the library's status code without
+    raising."""
     g = len(M)
     lib = load()
     arr = lambda vals, ct: (ct * g)(*vals)
-    fn = lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
+    fn = _entry(lib, blocked, fmt)
     return fn(
         g, arr([int(v) for v in M], ctypes.c_int), arr([int(v) for v in N], ctypes.c_int),
         arr([int(v) for v in K], ctypes.c_int),
@@ -103,11 +114,11 @@ class GroupGemmCall:
     per-call Python list work.  The addresses must stay valid while it is used.
     """
 
-    def __init__(self, M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False):
+    def __init__(self, M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False, fmt="nvfp4"):
         g = len(M)
         lib = load()
         arr = lambda vals, ct: (ct * g)(*vals)
-        self._fn = lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
+        self._fn = _entry(lib, blocked, fmt)
         self._args = (g, arr([int(v) for v in M], ctypes.c_int), arr([int(v) for v in N], ctypes.c_int),
                       arr([int(v) for v in K], ctypes.c_int), arr(A, ctypes.c_void_p),
                       arr(B, ctypes.c_void_p), arr(SFA, ctypes.c_void_p), arr(SFB, ctypes.c_void_p),
@@ -123,13 +134,13 @@ def blocked_scale_bytes(rows: int, K: int) -> int:
     return -(-rows // 128) * 128 * (-(-(K // 16) // 4) * 4)
 
 
-def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=False):
+def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=False, fmt="nvfp4"):
     """C_i = A_i . B_i^T for every group (see include/nvfp4gg.h).
 
     A, B, SFA, SFB: lists of contiguous uint8 device tensors holding the packed
     codes (A_i: M_i*K_i/2 bytes, SFA_i: M_i*K_i/16 bytes, ...; with
     blocked=True the scales are in the blocked layout, blocked_scale_bytes
-    each).
+    each; with fmt="mxfp4" they are E8M0, M_i*K_i/32 and N_i*K_i/32 bytes).
     C: list of contiguous float16 device tensors (M_i*N_i elements), written.
     M, N, K: sizes; taken from C's and A's shapes when omitted
     (C_i as (M_i, N_i), A_i as (M_i, K_i/2)).
@@ -144,8 +155,9 @@ def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=F
     if K is None:
         K = [int(a.shape[-1]) * 2 for a in A]
     for i in range(g):
-        sfa_n = blocked_scale_bytes(M[i], K[i]) if blocked else M[i] * K[i] // 16
-        sfb_n = blocked_scale_bytes(N[i], K[i]) if blocked else N[i] * K[i] // 16
+        per = 32 if fmt == "mxfp4" else 16
+        sfa_n = blocked_scale_bytes(M[i], K[i]) if blocked else M[i] * K[i] // per
+        sfb_n = blocked_scale_bytes(N[i], K[i]) if blocked else N[i] * K[i] // per
         need = {"A": (A[i], M[i] * K[i] // 2), "B": (B[i], N[i] * K[i] // 2),
                 "SFA": (SFA[i], sfa_n), "SFB": (SFB[i], sfb_n), "C": (C[i], M[i] * N[i])}
         for name, (t, n) in need.items():
@@ -156,7 +168,7 @@ def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=F
     psa = [_ptr(t, "SFA", _BYTES) for t in SFA]
     psb = [_ptr(t, "SFB", _BYTES) for t in SFB]
     pc = [_ptr(t, "C", ("float16",)) for t in C]
-    _check(group_gemm_ptrs(M, N, K, pa, pb, psa, psb, pc, _stream_handle(stream), blocked=blocked))
+    _check(group_gemm_ptrs(M, N, K, pa, pb, psa, psb, pc, _stream_handle(stream), blocked=blocked, fmt=fmt))
     return C
 
 

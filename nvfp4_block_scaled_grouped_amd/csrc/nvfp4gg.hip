@@ -161,13 +161,22 @@ struct AStage {
     h8_t v[kMaxAFrags][kKSteps][kWave];
 };
 
-// The workgroup's LDS: two A stages.  At the end of a segment the same
+// The workgroup's LDS: two A stages (dequantised fp16 for NVFP4, raw codes
+// for MXFP4).  At the end of a segment the same
 // memory carries the fp16 output tile on its way to C (rows padded by 16
 // bytes against bank conflicts).
 constexpr int kCTileStride = kTileN + 8;   // halves per LDS row of the output tile
+// MXFP4 kernel: the raw A codes of a stage in MFMA operand order (16 bytes
+// per lane per 16-row fragment) and each lane's E8M0 scale byte.
+struct MxStage {
+    i4_t v[kMaxAFrags][kWave];
+    uint32_t s[kMaxAFrags][kWave];
+};
+
 struct SharedMem {
     union {
         AStage a[2];
+        MxStage mx[2];
         uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
     };
     // Target of the A pieces of waves with a unit past the tile's fragments
@@ -343,6 +352,139 @@ __device__ __forceinline__ h2_t scales2(uint32_t sc, uint32_t shift)
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc >> shift, 1.0f, false);
 }
 
+// The end of a segment: chains of one segment meet in the scratch slot; the
+// last chain finishes the tile alone, or as one of several contributors
+// (partial-tile store, counter, and the fix-up by the last to arrive).
+// acc holds the wave's part of the segment's sum: acc[i][f] element r of lane
+// (c16, kq) is tile row 16 i + c16, column 32 wave + 16 f + 4 kq + r.
+template <int MF>
+__device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos& pos, bool first_chain,
+                                               bool last_chain, SharedMem& sm, int* s_flag, f4_t (*acc)[2],
+                                               int m0, int n0, int wave)
+{
+    const GroupSched& gs = args.sched[pos.group];
+    const GroupArgs& ga = args.grp[pos.group];
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
+    // Epilogue addresses, recomputed here rather than kept through the loop.
+    const uint32_t ewave_in_slot =
+        (uint32_t)wave * (kMaxAFrags * 2) * (kWave * 16u) + (uint32_t)(opaque_tid() % kWave) * 16u;
+    const uint32_t scratch_base =
+        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + ewave_in_slot;
+    // Chains of one segment meet in the scratch slot.
+    if (!first_chain) load_block<MF>(rP, scratch_base, acc);
+    if (!last_chain) {
+        store_block<MF>(rP, scratch_base, acc);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        return;
+    }
+
+    // Finish the tile: alone, or as one of several contributors.  Every
+    // wave holds its part of the segment's sum in acc.
+    const int unit = pos.unit;
+    const int64_t c_first = pos.tile_cost0;
+    const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
+    const int w_first = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_first));
+    const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
+    if (w_first == w_last) {
+        asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
+        return;
+    }
+    const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
+    const int tile = tile_index(args.sched, pos);
+    // Partial tile -> this workgroup's slot (partial_slot).  The stores carry
+    // the device-scope coherence bit (sc1), so they are written through past
+    // this XCD's L2; waiting for them before the counter update publishes
+    // them to whichever workgroup finishes the tile, with no cache flush.
+    auto slot_base = [&](int w) {
+        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + ewave_in_slot;
+    };
+    store_block<MF>(rP, slot_base(me), acc);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old =
+            __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = (old == w_last - w_first) ? 1 : 0;
+    }
+    __syncthreads();
+    const bool last = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+    __syncthreads();   // s_flag is reused by the next segment
+    if (!last) return;
+    // Sum the contributors' partials in workgroup order, so the result does
+    // not depend on who arrived last.  Loads carry the device-scope
+    // coherence bit; a contributor index past w_last gets an offset beyond
+    // the buffer, whose loads return zeros.
+    constexpr int kPieces = 4 * MF;
+    auto load_piece = [&](int w, int q) {
+        const uint32_t base = w <= w_last ? slot_base(w) : kNoSlot;
+        return __builtin_bit_cast(
+            f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
+    };
+    if (me == w_first) {
+        // This workgroup's partial is still in the accumulators (often the
+        // case: the first contributor ends its range with the tile's first
+        // stages, so it tends to finish last); the others are added to it,
+        // kChunk pieces of kBatch contributors in flight.  Tiles of 4 or more
+        // fragments take one contributor at a time (in two halves for 6
+        // fragments): their accumulators hold the registers.
+        constexpr int kChunk = MF <= 5 ? kPieces : kPieces / 2;
+        constexpr int kBatch = MF <= 3 ? 24 / kChunk : 1;
+        for (int w0 = w_first + 1; w0 <= w_last; w0 += kBatch) {
+#pragma unroll
+            for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+                f4_t v[kBatch][kChunk];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                        acc[(q0 + q) >> 1][(q0 + q) & 1] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("; fix-up, first contributor" ::: "memory");
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
+    } else {
+        // Every partial, this workgroup's own included, is read back, so the
+        // accumulators are free: kChunk pieces of kBatch contributors in
+        // flight, each summed chunk straight to the LDS copy of the tile.
+        constexpr int kChunk = MF <= 3 ? kPieces : kPieces / 2;
+        constexpr int kBatch = (MF <= 2 ? 32 : 24) / kChunk;
+        const int flane = opaque_tid() % kWave;
+#pragma unroll
+        for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+            f4_t sum[kChunk];
+#pragma unroll
+            for (int q = 0; q < kChunk; ++q) sum[q] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int w0 = w_first; w0 <= w_last; w0 += kBatch) {
+                f4_t v[kBatch][kChunk];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) sum[q] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                stage_c(sm, (q0 + q) >> 1, (q0 + q) & 1, sum[q], wave, flane);
+        }
+        asm volatile("; fix-up" ::: "memory");
+        write_c<MF>(sm, ga, m0, n0);
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
 // One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
 // stages (one chain for any K <= 8192); first_chain / last_chain place this
@@ -439,8 +581,6 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     }
 
     f4_t acc[NA][2];
-    const __amdgpu_buffer_rsrc_t rP =
-        make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
 
     {
         const int n = s_end - s_begin;
@@ -639,122 +779,217 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         if (i < n) stage(Parity<0>{}, i);
         if (kRing > 2 && i + 1 < n) stage(Parity<1>{}, i + 1);
     }
-    // Epilogue addresses, recomputed here rather than kept through the loop.
-    const uint32_t ewave_in_slot =
-        (uint32_t)wave * (kMaxAFrags * 2) * (kWave * 16u) + (uint32_t)(opaque_tid() % kWave) * 16u;
-    const uint32_t scratch_base =
-        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + ewave_in_slot;
-    // Chains of one segment meet in the scratch slot.
-    if (!first_chain) load_block<MF>(rP, scratch_base, acc);
-    if (!last_chain) {
-        store_block<MF>(rP, scratch_base, acc);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        return;
+    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
+}
+
+// ------------------------------------------------------------------ MXFP4
+//
+// MXFP4 operands: the same packed E2M1 codes, with one E8M0 scale (the value
+// 2^(code - 127)) per 32 consecutive K of a row, row-major M x K/32 and
+// N x K/32 bytes.  gfx950's block-scaled MFMA takes this form as it is:
+// v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands (format code 4)
+// multiplies each lane's 32 codes by that lane's E8M0 scale.  Lane (c16, kq)
+// supplies row c16 of an operand fragment and K = 32 kq .. 32 kq + 31 of the
+// 128-K step, which are bytes 16 kq .. 16 kq + 15 of the row's 64 bytes of
+// the stage, in the natural nibble order; its scale is byte 4 s + kq of the
+// row's scales at stage s.  No dequantisation, one MFMA per fragment pair
+// per stage.
+using v8i_t = int __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f4_t mfma_mx(i4_t b, uint32_t sb, i4_t a, uint32_t sa, f4_t c)
+{
+    const v8i_t bv = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+    const v8i_t av = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    // src0 = B fragment (output columns), src1 = A fragment (output rows),
+    // both FP4; scale byte 0 of each scale register.
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, 4, 4, 0, (int)sb, 0, (int)sa);
+}
+
+__device__ __forceinline__ uint32_t load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// Stages J .. R-1 of a ring pass: f(Parity<J>, i + J) for those below n.
+template <int J, int R, class F>
+__device__ __forceinline__ void ring_tail(F& f, int i, int n)
+{
+    if constexpr (J < R) {
+        if (i + J < n) {
+            f(Parity<J>{}, i + J);
+            ring_tail<J + 1, R>(f, i, n);
+        }
+    }
+}
+
+template <int J, int R, class F>
+__device__ __forceinline__ void ring_pass(F& f, int i)
+{
+    if constexpr (J < R) {
+        f(Parity<J>{}, i + J);
+        ring_pass<J + 1, R>(f, i);
+    }
+}
+
+// One segment of an MXFP4 tile (same tile shape, schedule, wave layout and
+// end of segment as run_segment):
+//   * B: each lane loads 16 bytes of its row per stage (the MFMA operand as
+//     it is) and its scale byte, kRing stages ahead in a register ring.
+//   * A: wave w loads fragment w (and w + 8 for more than 8 fragments) the
+//     same way, one stage ahead of its use, and stores it with its scale
+//     bytes into a double-buffered LDS stage that every wave reads.
+//   * Per stage each wave runs 2 x NA MFMAs of 16 x 16 x 128; one LDS-only
+//     barrier ends the stage.
+template <int MF>
+__device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
+                                               bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
+{
+    constexpr int NA = 2 * MF;
+    constexpr int kU = NA > kWaves ? 2 : 1;
+    // Stages of B in flight: the MFMAs take a fraction of what the B
+    // stream does, so the ring is as deep as the registers allow.
+    constexpr int kRing = MF <= 2 ? 8 : MF <= 4 ? 6 : 3;
+    // A fragments read from LDS per group (the scheduling barrier between
+    // groups keeps the compiler from loading every fragment of the stage up
+    // front, which large tiles have no registers for).
+    constexpr int kAGroup = MF <= 4 ? NA : 4;
+    const GroupSched& gs = args.sched[pos.group];
+    const GroupArgs& ga = args.grp[pos.group];
+    const int tid = opaque_tid();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int lane = tid % kWave;
+    const int c16 = lane & 15;
+    const int kq = lane >> 4;
+    const int M = ga.M, N = ga.N, K = ga.K;
+    const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
+    const int n0 = pos.nb * kTileN;
+    const uint32_t row_bytes = (uint32_t)K / 2;
+    const uint32_t row_scales = (uint32_t)K / 32;
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
+
+    // Rows past M or N are beyond the buffers and read zeros.
+    uint32_t offB[2], offSB[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
+        offB[f] = brow * row_bytes + 16u * kq;
+        offSB[f] = brow * row_scales + (uint32_t)kq;
+    }
+    uint32_t offA[2], offSA[2];
+#pragma unroll
+    for (int x = 0; x < kU; ++x) {
+        const int a = wave + kWaves * x;
+        const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);
+        offA[x] = arow * row_bytes + 16u * kq;
+        offSA[x] = arow * row_scales + (uint32_t)kq;
     }
 
-    // Finish the tile: alone, or as one of several contributors.  Every
-    // wave holds its part of the segment's sum in acc.
-    const int unit = pos.unit;
-    const int64_t c_first = pos.tile_cost0;
-    const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
-    const int w_first = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_first));
-    const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
-    if (w_first == w_last) {
-        asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
-        store_c<MF>(sm, ga, m0, n0, acc, wave);
-        return;
-    }
-    const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
-    const int tile = tile_index(args.sched, pos);
-    // Partial tile -> this workgroup's slot (partial_slot).  The stores carry
-    // the device-scope coherence bit (sc1), so they are written through past
-    // this XCD's L2; waiting for them before the counter update publishes
-    // them to whichever workgroup finishes the tile, with no cache flush.
-    auto slot_base = [&](int w) {
-        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + ewave_in_slot;
-    };
-    store_block<MF>(rP, slot_base(me), acc);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old =
-            __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = (old == w_last - w_first) ? 1 : 0;
-    }
-    __syncthreads();
-    const bool last = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
-    __syncthreads();   // s_flag is reused by the next segment
-    if (!last) return;
-    // Sum the contributors' partials in workgroup order, so the result does
-    // not depend on who arrived last.  Loads carry the device-scope
-    // coherence bit; a contributor index past w_last gets an offset beyond
-    // the buffer, whose loads return zeros.
-    constexpr int kPieces = 4 * MF;
-    auto load_piece = [&](int w, int q) {
-        const uint32_t base = w <= w_last ? slot_base(w) : kNoSlot;
-        return __builtin_bit_cast(
-            f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
-    };
-    if (me == w_first) {
-        // This workgroup's partial is still in the accumulators (often the
-        // case: the first contributor ends its range with the tile's first
-        // stages, so it tends to finish last); the others are added to it,
-        // kChunk pieces of kBatch contributors in flight.  Tiles of 4 or more
-        // fragments take one contributor at a time (in two halves for 6
-        // fragments): their accumulators hold the registers.
-        constexpr int kChunk = MF <= 5 ? kPieces : kPieces / 2;
-        constexpr int kBatch = MF <= 3 ? 24 / kChunk : 1;
-        for (int w0 = w_first + 1; w0 <= w_last; w0 += kBatch) {
+    f4_t acc[NA][2];
 #pragma unroll
-            for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
-                f4_t v[kBatch][kChunk];
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-                for (int b = 0; b < kBatch; ++b)
+        for (int f = 0; f < 2; ++f) acc[i][f] = zero_acc();
+
+    {
+        const int n = s_end - s_begin;
+        // Stage offsets in a row of codes and of scales; stages past the
+        // chain repeat its last stage (loaded, never used).
+        auto sbyte = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
+        };
+        auto sscl = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 32));
+        };
+        // A stores of waves whose unit is past the tile's fragments go to a
+        // discard area, so the stage has no branch (a branch would let the
+        // compiler sink each stage's MFMAs into later blocks).
+        i4_t* vdst[2];
+        uint32_t* sdst[2];
+        uint32_t mstep[2];
 #pragma unroll
-                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
-#pragma unroll
-                for (int b = 0; b < kBatch; ++b)
-#pragma unroll
-                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
-                        acc[(q0 + q) >> 1][(q0 + q) & 1] += v[b][q];
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int x = 0; x < kU; ++x) {
+            const int a = wave + kWaves * x;
+            const bool real = a < NA;
+            vdst[x] = real ? &sm.mx[0].v[a][lane] : reinterpret_cast<i4_t*>(&sm.discard[0][0]) + lane;
+            sdst[x] = real ? &sm.mx[0].s[a][lane]
+                           : reinterpret_cast<uint32_t*>(reinterpret_cast<i4_t*>(&sm.discard[0][0]) + kWave) + lane;
+            mstep[x] = real ? (uint32_t)sizeof(MxStage) : 0u;
         }
-        asm volatile("; fix-up, first contributor" ::: "memory");
-        store_c<MF>(sm, ga, m0, n0, acc, wave);
-    } else {
-        // Every partial, this workgroup's own included, is read back, so the
-        // accumulators are free: kChunk pieces of kBatch contributors in
-        // flight, each summed chunk straight to the LDS copy of the tile.
-        constexpr int kChunk = MF <= 3 ? kPieces : kPieces / 2;
-        constexpr int kBatch = (MF <= 2 ? 32 : 24) / kChunk;
-        const int flane = opaque_tid() % kWave;
+        auto put_a = [&](int buf, int x, i4_t v, uint32_t sc) {
+            *reinterpret_cast<i4_t*>(reinterpret_cast<char*>(vdst[x]) + buf * mstep[x]) = v;
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sdst[x]) + buf * mstep[x]) = sc;
+        };
+
+        i4_t bq[kRing][2], aq[kRing][2];
+        uint32_t bs[kRing][2], as[kRing][2];
+        {
+            i4_t a0[2];
+            uint32_t s0[2];
 #pragma unroll
-        for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
-            f4_t sum[kChunk];
+            for (int x = 0; x < kU; ++x) {
+                a0[x] = load16(rA, offA[x], sbyte(0));
+                s0[x] = load_u8(rSA, offSA[x], sscl(0));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int q = 0; q < kChunk; ++q) sum[q] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            for (int w0 = w_first; w0 <= w_last; w0 += kBatch) {
-                f4_t v[kBatch][kChunk];
+            for (int j = 0; j < kRing; ++j) {
 #pragma unroll
-                for (int b = 0; b < kBatch; ++b)
+                for (int f = 0; f < 2; ++f) {
+                    bq[j][f] = load16(rB, offB[f], sbyte(j));
+                    bs[j][f] = load_u8(rSB, offSB[f], sscl(j));
+                }
 #pragma unroll
-                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
-#pragma unroll
-                for (int b = 0; b < kBatch; ++b)
-#pragma unroll
-                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) sum[q] += v[b][q];
+                for (int x = 0; x < kU; ++x) {
+                    aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
+                    as[j][x] = load_u8(rSA, offSA[x], sscl(j + 1));
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
-                stage_c(sm, (q0 + q) >> 1, (q0 + q) & 1, sum[q], wave, flane);
+            for (int x = 0; x < kU; ++x) put_a(0, x, a0[x], s0[x]);
         }
-        asm volatile("; fix-up" ::: "memory");
-        write_c<MF>(sm, ga, m0, n0);
+        lds_barrier();
+
+        auto stage = [&](auto parity, int i) {
+            constexpr int p = decltype(parity)::value;
+            const int lb = i & 1;
+#pragma unroll
+            for (int a0 = 0; a0 < NA; a0 += kAGroup) {
+#pragma unroll
+                for (int a = a0; a < a0 + kAGroup && a < NA; ++a) {
+                    const i4_t av = sm.mx[lb].v[a][lane];
+                    const uint32_t sa = sm.mx[lb].s[a][lane];
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) acc[a][f] = mfma_mx(bq[p][f], bs[p][f], av, sa, acc[a][f]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // A of stage i + 1 into the other buffer (its readers of stage
+            // i - 1 passed the previous barrier), then the ring slot's
+            // reloads: B of stage i + kRing, A of stage i + 1 + kRing.
+#pragma unroll
+            for (int x = 0; x < kU; ++x) put_a(lb ^ 1, x, aq[p][x], as[p][x]);
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                bq[p][f] = load16(rB, offB[f], sbyte(i + kRing));
+                bs[p][f] = load_u8(rSB, offSB[f], sscl(i + kRing));
+            }
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                aq[p][x] = load16(rA, offA[x], sbyte(i + 1 + kRing));
+                as[p][x] = load_u8(rSA, offSA[x], sscl(i + 1 + kRing));
+            }
+            lds_barrier();
+        };
+        int i = 0;
+        for (; i + kRing - 1 < n; i += kRing) ring_pass<0, kRing>(stage, i);
+        ring_tail<0, kRing>(stage, i, n);
     }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(args.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
 // Wave-uniform values computed in vector registers (64-bit divisions have
@@ -781,11 +1016,12 @@ __device__ __forceinline__ Pos uniform(const Pos& p)
     return r;
 }
 
-__global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
+// The persistent walk of one workgroup over its cost range: every segment
+// (a tile's stages in the range) as chains of at most kMaxChainStages
+// stages, each by the segment kernel of its fragment count.
+template <bool kMx>
+__device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
-    __shared__ SharedMem sm;
-    __shared__ int s_flag;
-
     const int w = uniform(worker_id(args.G));
     const int64_t b1 = uniform(boundary(args.W, args.G, w + 1));
     Pos pos = uniform(locate(args.sched, args.ngroups, uniform(boundary(args.W, args.G, w))));
@@ -799,18 +1035,43 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
         for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
             const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
             const bool first = c0 == pos.stage, last = c1 == s_end;
-            switch (pos.frags) {
-                case 1: run_segment<1>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                case 2: run_segment<2>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                case 3: run_segment<3>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                case 4: run_segment<4>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                case 5: run_segment<5>(args, pos, c0, c1, first, last, sm, &s_flag); break;
-                default: run_segment<6>(args, pos, c0, c1, first, last, sm, &s_flag); break;
+            if constexpr (kMx) {
+                switch (pos.frags) {
+                    case 1: run_segment_mx<1>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 2: run_segment_mx<2>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 3: run_segment_mx<3>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 4: run_segment_mx<4>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 5: run_segment_mx<5>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    default: run_segment_mx<6>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                }
+            } else {
+                switch (pos.frags) {
+                    case 1: run_segment<1>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 2: run_segment<2>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 3: run_segment<3>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 4: run_segment<4>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 5: run_segment<5>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    default: run_segment<6>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                }
             }
         }
         if (s_end < gs.stages) break;
         pos = uniform(locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages));
     }
+}
+
+__global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
+{
+    __shared__ SharedMem sm;
+    __shared__ int s_flag;
+    walk_range<false>(args, sm, &s_flag);
+}
+
+__global__ __launch_bounds__(kThreads) void mxfp4_group_gemm_kernel(const LaunchArgs args)
+{
+    __shared__ SharedMem sm;
+    __shared__ int s_flag;
+    walk_range<true>(args, sm, &s_flag);
 }
 
 // Writes zeros to C of a group with K == 0 (the empty sum).
@@ -928,14 +1189,15 @@ int device_cus(int dev)
 
 extern "C" const char* nvfp4_group_gemm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int nvfp4_group_gemm_version(void) { return 2; }
+extern "C" int nvfp4_group_gemm_version(void) { return 3; }
 
 namespace {
 
-// Both entry points: blocked_sf selects the layout of the scale arrays.
+// Every grouped-GEMM entry point: fmt selects NVFP4 (E4M3 per 16 K) or
+// MXFP4 (E8M0 per 32 K), blocked_sf the blocked layout of NVFP4 scales.
 int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void* const* A_ptrs,
                     const void* const* B_ptrs, const void* const* SFA_ptrs, const void* const* SFB_ptrs,
-                    void* const* C_ptrs, void* stream, int blocked_sf)
+                    void* const* C_ptrs, void* stream, int blocked_sf, int fmt)
 {
     g_last_error.clear();
     if (g <= 0) return fail(NVFP4GG_INVALID_ARG, "g must be >= 1");
@@ -1001,7 +1263,7 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
             ++n;
         }
         if (n == 0) continue;
-        const int maxf = choose_max_frags(n, bM, bN, bK, cus);
+        const int maxf = choose_max_frags(n, bM, bN, bK, cus, fmt);
         int tiles = 0;
         int64_t cost = 0;
         for (int j = 0; j < n; ++j) {
@@ -1016,7 +1278,7 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
             ga.M = M[q];
             ga.N = N[q];
             ga.K = K[q];
-            sc = make_group_sched(M[q], N[q], K[q], cost, tiles, maxf);
+            sc = make_group_sched(M[q], N[q], K[q], cost, tiles, maxf, fmt);
             cost += group_cost(sc);
             tiles += sc.mblocks * sc.nblocks;
         }
@@ -1031,7 +1293,10 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         if (rc != NVFP4GG_OK) return rc;
         args.partials = ws.partials;
         args.counters = ws.counters;
-        hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
+        if (fmt == kFmtMxfp4)
+            hipLaunchKernelGGL(mxfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
+        else
+            hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -1046,7 +1311,7 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
                                 const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                                 void* const* C_ptrs, void* stream)
 {
-    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0);
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0, kFmtNvfp4);
 }
 
 extern "C" int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,
@@ -1054,7 +1319,14 @@ extern "C" int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const
                                         const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                                         void* const* C_ptrs, void* stream)
 {
-    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 1);
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 1, kFmtNvfp4);
+}
+
+extern "C" int mxfp4_group_gemm(int g, const int* M, const int* N, const int* K, const void* const* A_ptrs,
+                                const void* const* B_ptrs, const void* const* SFA_ptrs,
+                                const void* const* SFB_ptrs, void* const* C_ptrs, void* stream)
+{
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0, kFmtMxfp4);
 }
 
 extern "C" int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX, void* out, void* stream)

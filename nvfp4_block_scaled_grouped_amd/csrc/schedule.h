@@ -16,10 +16,12 @@
 //     n-block, then m-block, so the m-blocks that share a B strip are
 //     adjacent in the order.
 //   * stage: kStageK consecutive K of a tile.  A stage of a tile with f
-//     fragments costs unit_cost(f) units (about 50 ns of MI355X time each,
-//     fitted to measured stage times): the B stream and its dequantisation
-//     do not grow with f, the MFMAs do, and tiles of more than 4 fragments
-//     give every wave a second piece of A to dequantise.
+//     fragments costs unit_cost(f, fmt) units (about 50 ns of MI355X time
+//     each, fitted to measured stage times).  NVFP4 (fp16 MFMA after
+//     dequantisation): the B stream and its dequantisation do not grow with
+//     f, the MFMAs do, and tiles of more than 4 fragments give every wave a
+//     second piece of A to dequantise.  MXFP4 (native FP4 MFMA, no
+//     dequantisation): a stage is mostly its B stream.
 //   * A tile's cost range is kTileCost (the start-up and wind-down of the
 //     segment that starts it: first loads, partial-tile stores, the fix-up)
 //     followed by its stages.
@@ -44,7 +46,9 @@ constexpr int kTileN = 256;        // columns per n-block
 constexpr int kStageK = 128;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
 constexpr int kTileCost = 200;     // cost units of a tile beyond its stages
-constexpr int kMaxUnitCost = 56;   // the costliest stage (6 fragments)
+constexpr int kMaxUnitCost = 56;   // the costliest stage (NVFP4, 6 fragments)
+constexpr int kFmtNvfp4 = 0;       // E4M3 scale per 16 K, fp16 MFMA
+constexpr int kFmtMxfp4 = 1;       // E8M0 scale per 32 K, FP4 MFMA
 // Least cost handed to one workgroup: keeps every workgroup range longer
 // than the costliest stage, so the workgroups sharing a tile are
 // consecutive.
@@ -58,17 +62,20 @@ struct GroupSched {
     int nblocks;          // ceil(N / kTileN)
     int stages;           // K / kStageK
     int tile_begin;       // tiles before this group
+    int fmt;              // kFmtNvfp4 or kFmtMxfp4 (selects the stage costs)
 };
 
 NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
 // The schedule entry of a group with M, N >= 1 and K a positive multiple of
 // kStageK, in m-blocks of at most maxf (1..kMaxFrags) fragments.
-NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin, int maxf = kMaxFrags)
+NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin, int maxf = kMaxFrags,
+                                     int fmt = kFmtNvfp4)
 {
     GroupSched g;
     g.cost_begin = cost_begin;
     g.tile_begin = tile_begin;
+    g.fmt = fmt;
     g.frags = ceil_div_i(M, kFragRows);
     g.mblocks = ceil_div_i(g.frags, maxf);
     g.nblocks = ceil_div_i(N, kTileN);
@@ -77,10 +84,12 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 }
 
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
-// about 50 ns (measured MI355X stage times: 1.2, 1.45, 1.75, 2.3 and 2.8 us
-// for 2 to 6 fragments; one fragment extrapolated).
-NVFP4_HD int unit_cost(int f)
+// about 50 ns.  NVFP4: measured MI355X stage times 1.2, 1.45, 1.75, 2.3 and
+// 2.8 us for 2 to 6 fragments, one fragment extrapolated.  MXFP4: stage
+// times of its kernel (about 0.5 to 0.8 us).
+NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
+    if (fmt == kFmtMxfp4) return f <= 2 ? 10 : f <= 4 ? 12 : 15;
     return f <= 1 ? 21 : f == 2 ? 24 : f == 3 ? 29 : f == 4 ? 35 : f == 5 ? 46 : kMaxUnitCost;
 }
 
@@ -104,7 +113,8 @@ NVFP4_HD int64_t mblock_cost0(const GroupSched& g, int i)
 {
     const int base = g.frags / g.mblocks, extra = g.frags % g.mblocks;
     const int big = i < extra ? i : extra;             // m-blocks of base + 1 fragments before i
-    const int64_t stage_sum = (int64_t)(i - big) * unit_cost(base) + (int64_t)big * unit_cost(base + 1);
+    const int64_t stage_sum =
+        (int64_t)(i - big) * unit_cost(base, g.fmt) + (int64_t)big * unit_cost(base + 1, g.fmt);
     return (int64_t)kTileCost * i + stage_sum * g.stages;
 }
 
@@ -147,7 +157,7 @@ NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
         while (mb + 1 < g.mblocks && mblock_cost0(g, mb + 1) <= q) ++mb;
         r.mb = mb;
         r.frags = mblock_frags(g.frags, g.mblocks, mb);
-        r.unit = unit_cost(r.frags);
+        r.unit = unit_cost(r.frags, g.fmt);
         const int64_t mcost0 = mblock_cost0(g, mb);
         q -= mcost0 + kTileCost;   // relative to the start of stage 0
         r.stage = q <= 0 ? 0 : (int)((q + r.unit - 1) / r.unit);
@@ -194,7 +204,7 @@ inline double launch_estimate(int64_t W, int G, int tiles)
 // Large m-blocks stream each B strip once and run the MFMAs densest; smaller
 // ones give problems with few tiles more of them, so fewer workgroups share
 // a tile.
-inline int choose_max_frags(int n, const int* M, const int* N, const int* K, int cus)
+inline int choose_max_frags(int n, const int* M, const int* N, const int* K, int cus, int fmt = kFmtNvfp4)
 {
     int best = kMaxFrags;
     double best_t = 0.0;
@@ -202,7 +212,7 @@ inline int choose_max_frags(int n, const int* M, const int* N, const int* K, int
         int64_t W = 0;
         int tiles = 0;
         for (int i = 0; i < n; ++i) {
-            const GroupSched g = make_group_sched(M[i], N[i], K[i], W, tiles, maxf);
+            const GroupSched g = make_group_sched(M[i], N[i], K[i], W, tiles, maxf, fmt);
             W += group_cost(g);
             tiles += g.mblocks * g.nblocks;
         }

@@ -94,6 +94,69 @@ def round_f16_double(x: float) -> int:
     return int(_load().oracle_round_f16_double(float(x)))
 
 
+def e8m0(code: int) -> float:
+    lib = _load()
+    lib.oracle_e8m0.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0.restype = ctypes.c_double
+    return float(lib.oracle_e8m0(int(code)))
+
+
+def mx_group_gemm(M, N, K, A, B, SFA, SFB, *, exact: bool = False, nthreads: int = 0):
+    """The MXFP4 oracle (E8M0 scales, M_i x K_i/32 and N_i x K_i/32 bytes).
+    Returns the fp16 outputs, plus the exact sums when ``exact`` is set."""
+    g = len(M)
+    lib = _load()
+    pp = ctypes.POINTER(ctypes.c_void_p)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_mx_group_gemm.argtypes = [ctypes.c_int, ip, ip, ip, pp, pp, pp, pp, pp, pp, ctypes.c_int]
+    lib.oracle_mx_group_gemm.restype = ctypes.c_int
+    keep = []
+
+    def ptrs(arrs):
+        out = (ctypes.c_void_p * g)()
+        for i, a in enumerate(arrs):
+            keep.append(a)
+            out[i] = a.ctypes.data
+        return out
+
+    A = [np.ascontiguousarray(a, dtype=np.uint8) for a in A]
+    B = [np.ascontiguousarray(a, dtype=np.uint8) for a in B]
+    SFA = [np.ascontiguousarray(a, dtype=np.uint8) for a in SFA]
+    SFB = [np.ascontiguousarray(a, dtype=np.uint8) for a in SFB]
+    for i in range(g):
+        if (A[i].size != M[i] * K[i] // 2 or B[i].size != N[i] * K[i] // 2
+                or SFA[i].size != M[i] * K[i] // 32 or SFB[i].size != N[i] * K[i] // 32):
+            raise ValueError("oracle.mx_group_gemm: group %d has wrong byte counts" % i)
+    C = [np.empty((M[i], N[i]), dtype=np.uint16) for i in range(g)]
+    X = [np.empty((M[i], N[i]), dtype=np.float64) for i in range(g)] if exact else None
+    rc = lib.oracle_mx_group_gemm(g, (ctypes.c_int * g)(*M), (ctypes.c_int * g)(*N), (ctypes.c_int * g)(*K),
+                                  ptrs(A), ptrs(B), ptrs(SFA), ptrs(SFB), ptrs(C),
+                                  ptrs(X) if exact else None, int(nthreads))
+    if rc == -2:
+        raise ValueError("oracle_mx_group_gemm: scale exponents spread too wide for the exact sum")
+    if rc != 0:
+        raise ValueError("oracle_mx_group_gemm: bad sizes")
+    C = [c.view(np.float16) for c in C]
+    return (C, X) if exact else C
+
+
+def mx_gemm_element(M, N, K, A, B, SFA, SFB, m, n):
+    """One MXFP4 output element of a single group: (fp16 bits, exact value)."""
+    lib = _load()
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    lib.oracle_mx_gemm_element.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, u8p, u8p, u8p, u8p,
+                                           ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_uint16),
+                                           ctypes.POINTER(ctypes.c_double)]
+    lib.oracle_mx_gemm_element.restype = ctypes.c_int
+    c16 = ctypes.c_uint16()
+    ex = ctypes.c_double()
+    rc = lib.oracle_mx_gemm_element(int(M), int(N), int(K), _u8ptr(A), _u8ptr(B), _u8ptr(SFA), _u8ptr(SFB),
+                                    int(m), int(n), ctypes.byref(c16), ctypes.byref(ex))
+    if rc != 0:
+        raise ValueError("oracle_mx_gemm_element: bad index or exponent spread")
+    return int(c16.value), float(ex.value)
+
+
 def blocked_scale_bytes(rows: int, cols: int) -> int:
     """Size of the blocked layout of a rows x cols scale matrix."""
     lib = _load()

@@ -254,6 +254,145 @@ int oracle_dequant(int rows, int K, const uint8_t* X, const uint8_t* SFX, double
     return 0;
 }
 
+/* ------------------------------------------------------------------- MXFP4
+ *
+ * The MX form of the product (page 505431 names MX block scaling beside the
+ * NVFP4 one: one block-scaled MMA kind covers both, and its instruction
+ * descriptor has a scale-type field; page 444497's header comment speaks of
+ * MX block scaling).  The pages do not define it; it is read as the OCP MX
+ * format: the same E2M1 codes, one E8M0 scale per 32 consecutive K of a row,
+ * E8M0 an unsigned 8-bit exponent with value 2^(code - 127) and code 0xFF
+ * NaN.  For every group, row m and column n:
+ *
+ *     C[m][n] = fp16( sum_k a(m,k) 2^(sa(m,k/32) - 127) b(n,k) 2^(sb(n,k/32) - 127) )
+ *
+ * formed exactly and rounded once (round-to-nearest-even, overflow to inf). */
+double oracle_e8m0(uint8_t code)
+{
+    if (code == 0xFF) return NAN;
+    return ldexp(1.0, (int)code - 127);
+}
+
+/* Exact dot product.  A term is (2a)(2b) 2^(ea + eb - 256), (2a)(2b) an
+ * integer of magnitude <= 144 (oracle_e2m1_x2).  With Emin the least
+ * exponent sum ea + eb along the row pair, the sum is S 2^(Emin - 256) with S
+ * an integer, accumulated in __int128 as long as no term is shifted by more
+ * than 96 bits (K <= 2^20 then keeps |S| < 2^124).  Returns 0 and (S, E =
+ * Emin - 256), 1 if a scale is NaN, -1 if the exponent spread is too wide. */
+static int mx_dot(const uint8_t* arow, const uint8_t* sarow, const uint8_t* brow,
+                  const uint8_t* sbrow, int64_t K, __int128* S, int* E)
+{
+    int emin = 1 << 30;
+    for (int64_t b = 0; b < K / 32; ++b) {
+        if (sarow[b] == 0xFF || sbrow[b] == 0xFF) return 1;
+        const int e = (int)sarow[b] + (int)sbrow[b];
+        if (e < emin) emin = e;
+    }
+    __int128 s = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        const int shift = (int)sarow[k / 32] + (int)sbrow[k / 32] - emin;
+        if (shift > 96) return -1;
+        const int p = oracle_e2m1_x2(fp4_at(arow, k)) * oracle_e2m1_x2(fp4_at(brow, k));
+        s += (__int128)p * ((__int128)1 << shift);
+    }
+    *S = s;
+    *E = emin - 256;
+    return 0;
+}
+
+/* S 2^E rounded once to fp16: round-to-nearest-even on the integer itself,
+ * overflow to inf, underflow to a signed zero, an exact zero to +0 (the same
+ * rules as oracle_round_f16_fixed20, for any binary exponent).  *exact gets
+ * S 2^E as a double (rounded if S needs more than 53 bits). */
+static uint16_t round_f16_int128(__int128 S, int E, double* exact)
+{
+    if (S == 0) {
+        if (exact) *exact = 0.0;
+        return 0;
+    }
+    const uint16_t sign = S < 0 ? 0x8000 : 0;
+    const unsigned __int128 u = S < 0 ? (unsigned __int128)(-S) : (unsigned __int128)S;
+    if (exact) *exact = (sign ? -1.0 : 1.0) * ldexp((double)u, E);
+    int e = 0;                                  /* u in [2^e, 2^(e+1)) */
+    while ((u >> e) > 1) ++e;
+    const int V = e + E;                        /* unbiased exponent of the value */
+    const int qexp = V >= -14 ? V - 10 : -24;   /* exponent of the last kept bit */
+    const int shift = qexp - E;                 /* bits of u below it */
+    unsigned __int128 q;
+    if (shift <= 0) {
+        q = u << (-shift);
+    } else if (shift >= 126) {
+        q = 0;                                  /* below half the smallest subnormal */
+    } else {
+        const unsigned __int128 rem = u & (((unsigned __int128)1 << shift) - 1);
+        const unsigned __int128 half = (unsigned __int128)1 << (shift - 1);
+        q = u >> shift;
+        if (rem > half || (rem == half && (q & 1))) q++;
+    }
+    if (V < -14) return (uint16_t)(sign | (uint16_t)q);   /* subnormal; q == 1024 is the least normal */
+    int Ve = V;
+    if (q == 2048) {
+        q = 1024;
+        ++Ve;
+    }
+    if (Ve > 15) return (uint16_t)(sign | 0x7C00);
+    return (uint16_t)(sign | (uint16_t)((Ve + 15) << 10) | (uint16_t)(q - 1024));
+}
+
+/* One output element of an MXFP4 group: fp16 bits and the exact value (as a
+ * double).  A NaN scale gives NaN; a too-wide exponent spread returns -2. */
+int oracle_mx_gemm_element(int M, int N, int K, const uint8_t* A, const uint8_t* B, const uint8_t* SFA,
+                           const uint8_t* SFB, int m, int n, uint16_t* c16, double* exact)
+{
+    if (m < 0 || m >= M || n < 0 || n >= N || K % 32 != 0) return -1;
+    __int128 S;
+    int E;
+    const int rc = mx_dot(A + (int64_t)m * (K / 2), SFA + (int64_t)m * (K / 32), B + (int64_t)n * (K / 2),
+                          SFB + (int64_t)n * (K / 32), K, &S, &E);
+    if (rc < 0) return -2;
+    if (rc == 1) {
+        *c16 = 0x7E00;
+        *exact = NAN;
+        return 0;
+    }
+    *c16 = round_f16_int128(S, E, exact);
+    return 0;
+}
+
+/* The MXFP4 grouped GEMM (layouts as oracle_group_gemm, scales M x K/32 and
+ * N x K/32).  Returns -2 if some dot product's exponent spread is too wide
+ * for the exact sum. */
+int oracle_mx_group_gemm(int g, const int* M, const int* N, const int* K, const uint8_t* const* A,
+                         const uint8_t* const* B, const uint8_t* const* SFA, const uint8_t* const* SFB,
+                         uint16_t* const* C, double* const* Cexact, int nthreads)
+{
+    if (g < 0) return -1;
+    for (int i = 0; i < g; ++i)
+        if (M[i] < 0 || N[i] < 0 || K[i] < 0 || K[i] % 32 != 0) return -1;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+    for (int i = 0; i < g; ++i) {
+        const int64_t Mi = M[i], Ni = N[i], Ki = K[i];
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+        for (int64_t m = 0; m < Mi; ++m) {
+            for (int64_t n = 0; n < Ni; ++n) {
+                uint16_t c;
+                double x;
+                if (oracle_mx_gemm_element(M[i], N[i], K[i], A[i], B[i], SFA[i], SFB[i], (int)m, (int)n, &c, &x) != 0)
+                    bad = 1;
+                C[i][m * Ni + n] = c;
+                if (Cexact) Cexact[i][m * Ni + n] = x;
+            }
+        }
+        (void)Ki;
+    }
+    return bad ? -2 : 0;
+}
+
 /* ------------------------------------------------------ blocked scale layout
  *
  * The layout the pages' kernels read their scales in (page 482006, function

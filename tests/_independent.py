@@ -63,3 +63,34 @@ def brute_group(A, B, SFA, SFB, M, N, K):
 def pack_fp4(codes: np.ndarray) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def decode_mx(packed, scales, rows, K) -> np.ndarray:
+    """MXFP4 values: table value times 2^(code - 127) of the row's scale for
+    k // 32 (the power of two from Python's float exponentiation)."""
+    codes = unpack_fp4(packed, rows, K)
+    vals = e2m1_table()[codes]
+    sc = np.array([2.0 ** (int(c) - 127) for c in range(255)] + [np.nan])[
+        np.asarray(scales, dtype=np.uint8).reshape(rows, K // 32)]
+    return vals * np.repeat(sc, 32, axis=1)
+
+
+def brute_mx_group(A, B, SFA, SFB, M, N, K):
+    """fp16 result of one MXFP4 group by float64 matmul + numpy rounding
+    (exact while the scale exponents of a dot product stay within a few
+    dozen binades, as in the shapes the pins use)."""
+    exact = decode_mx(A, SFA, M, K) @ decode_mx(B, SFB, N, K).T
+    return exact.astype(np.float16), exact
+
+
+def exact_mx_element(a_codes, a_scales, b_codes, b_scales):
+    """One MXFP4 dot product as an exact Python fraction (codes per K, E8M0
+    scale codes per 32 K), for exponent spreads float64 cannot hold."""
+    from fractions import Fraction
+    t = e2m1_table()
+    s = Fraction(0)
+    for k in range(len(a_codes)):
+        ea = int(a_scales[k // 32]) - 127
+        eb = int(b_scales[k // 32]) - 127
+        s += Fraction(t[a_codes[k]]) * Fraction(t[b_codes[k]]) * Fraction(2) ** (ea + eb)
+    return s

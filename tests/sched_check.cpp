@@ -15,7 +15,8 @@ using namespace nvfp4sched;
 static int fails = 0;
 #define CHECK(c, ...) do { if (!(c)) { ++fails; std::printf("FAIL %s:%d: ", __FILE__, __LINE__); std::printf(__VA_ARGS__); std::printf("\n"); return; } } while (0)
 
-static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus, int maxf)
+static void run_case(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus, int maxf,
+                     int fmt)
 {
     int ng = (int)M.size();
     CHECK(maxf >= 1 && maxf <= kMaxFrags, "m-block size %d", maxf);
@@ -23,7 +24,7 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
     int64_t cost = 0;
     int tiles = 0;
     for (int i = 0; i < ng; ++i) {
-        gs[i] = make_group_sched(M[i], N[i], K[i], cost, tiles, maxf);
+        gs[i] = make_group_sched(M[i], N[i], K[i], cost, tiles, maxf, fmt);
         cost += group_cost(gs[i]);
         tiles += gs[i].mblocks * gs[i].nblocks;
         // m-block partition covers all fragments, each block 1..maxf, sizes
@@ -44,7 +45,7 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
         for (int b = 0; b <= gs[i].mblocks; ++b) {
             CHECK(mblock_cost0(gs[i], b) == c, "mblock_cost0 group %d block %d", i, b);
             if (b < gs[i].mblocks)
-                c += kTileCost + (int64_t)gs[i].stages * unit_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b));
+                c += kTileCost + (int64_t)gs[i].stages * unit_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b), fmt);
         }
     }
     const int64_t W = cost;
@@ -63,7 +64,7 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
             CHECK(++guard < 1000000, "runaway walk");
             const GroupSched& g = gs[pos.group];
             const int unit = pos.unit;
-            CHECK(unit == unit_cost(pos.frags), "unit cost");
+            CHECK(unit == unit_cost(pos.frags, fmt), "unit cost");
             const int64_t s_end64 = (b1 - pos.tile_cost0 + unit - 1) / unit;
             const int s_end = s_end64 < g.stages ? (int)s_end64 : g.stages;
             CHECK(s_end > pos.stage, "empty segment w=%d", w);
@@ -106,10 +107,11 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
 }
 
 // The launch's m-block size as the host picks it, then the schedule check.
-static void run_launch(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus)
+static void run_launch(const std::vector<int>& M, const std::vector<int>& N, const std::vector<int>& K, int cus,
+                       int fmt)
 {
-    const int maxf = choose_max_frags((int)M.size(), M.data(), N.data(), K.data(), cus);
-    run_case(M, N, K, cus, maxf);
+    const int maxf = choose_max_frags((int)M.size(), M.data(), N.data(), K.data(), cus, fmt);
+    run_case(M, N, K, cus, maxf, fmt);
 }
 
 int main()
@@ -122,10 +124,11 @@ int main()
         {{40, 76, 168, 72, 164, 148, 196, 160}, std::vector<int>(8, 7168), std::vector<int>(8, 2048)},
         {{80, 176, 128, 72, 64, 248, 96, 160}, std::vector<int>(8, 4096), std::vector<int>(8, 7168)},
     };
-    for (const auto& w : five) {
-        run_launch(w[0], w[1], w[2], 256);
-        for (int maxf = 1; maxf <= kMaxFrags; ++maxf) run_case(w[0], w[1], w[2], 256, maxf);
-    }
+    for (int fmt : {kFmtNvfp4, kFmtMxfp4})
+        for (const auto& w : five) {
+            run_launch(w[0], w[1], w[2], 256, fmt);
+            for (int maxf = 1; maxf <= kMaxFrags; ++maxf) run_case(w[0], w[1], w[2], 256, maxf, fmt);
+        }
     // Random shapes, grid sizes and m-block sizes.
     std::mt19937 rng(12345);
     for (int it = 0; it < 3000; ++it) {
@@ -137,10 +140,11 @@ int main()
             K.push_back(kStageK * (1 + rng() % 24));
         }
         const int cus = 1 + rng() % 300;
+        const int fmt = (it / 2) % 2 ? kFmtMxfp4 : kFmtNvfp4;
         if (it % 2 == 0)
-            run_launch(M, N, K, cus);
+            run_launch(M, N, K, cus, fmt);
         else
-            run_case(M, N, K, cus, 1 + rng() % kMaxFrags);
+            run_case(M, N, K, cus, 1 + rng() % kMaxFrags, fmt);
         if (fails) break;
     }
     if (fails) { std::printf("FAILED %d\n", fails); return 1; }

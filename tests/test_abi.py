@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert nv.version() == 2
+    assert nv.version() == 3
 
 
 A16 = 0x10000          # fake, aligned addresses: never dereferenced, every case
@@ -127,3 +127,11 @@ def test_blocked_scale_bytes():
     assert nv.blocked_scale_bytes(1, 128) == 128 * 8
     assert nv.blocked_scale_bytes(128, 7168) == 128 * 448
     assert nv.blocked_scale_bytes(129, 256) == 256 * 16
+
+
+def test_mxfp4_entry_validates(lib):
+    assert lib.mxfp4_group_gemm(0, None, None, None, None, None, None, None, None, None) == nv.INVALID_ARG
+    rc = nv.group_gemm_ptrs([8], [8], [144], [A16], [A16], [A16], [A16], [A16], 0, fmt="mxfp4")
+    assert rc == nv.UNSUPPORTED and "K % 128" in nv.last_error()
+    rc = nv.group_gemm_ptrs([8], [8], [256], [MIS], [A16], [A16], [A16], [A16], 0, fmt="mxfp4")
+    assert rc == nv.INVALID_ARG

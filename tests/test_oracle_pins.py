@@ -335,3 +335,126 @@ def test_blocked_pins_detect_plausible_mistakes(oracle_lib):
     row_first = 512 * ((s // 4) * 2 + r // 128) + 16 * (r % 32) + 4 * ((r // 32) % 4) + s % 4
     assert not np.array_equal(swapped, off)
     assert not np.array_equal(row_first, off)
+
+
+# ------------------------------------------------------------------- MXFP4
+
+def test_e8m0_closed_form(oracle_lib):
+    assert oracle_lib.e8m0(127) == 1.0
+    assert oracle_lib.e8m0(128) == 2.0
+    assert oracle_lib.e8m0(126) == 0.5
+    assert oracle_lib.e8m0(0) == 2.0 ** -127
+    assert oracle_lib.e8m0(254) == 2.0 ** 127
+    assert math.isnan(oracle_lib.e8m0(255))
+    for c in range(254):
+        assert oracle_lib.e8m0(c + 1) == 2.0 * oracle_lib.e8m0(c)
+
+
+@pytest.mark.parametrize("dist", ["pos", "unit"])
+@pytest.mark.parametrize("shape", [(1, 1, 32), (3, 5, 64), (8, 8, 128), (7, 4, 96)])
+def test_mx_bruteforce(oracle_lib, dist, shape):
+    """float64 matmul is exact here: products of two E2M1 values scaled by at
+    most 2^+-6, summed over at most 128 terms."""
+    M, N, K = shape
+    A, B, SA, SB = workloads.make_mx_inputs([M], [N], [K], 9, dist=dist)
+    want16, want = ind.brute_mx_group(A[0], B[0], SA[0], SB[0], M, N, K)
+    C, X = oracle_lib.mx_group_gemm([M], [N], [K], A, B, SA, SB, exact=True)
+    np.testing.assert_array_equal(X[0], want)
+    np.testing.assert_array_equal(C[0].view(np.uint16), want16.view(np.uint16))
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 64), (4, 3, 128)])
+def test_mx_wide_scales_exact(oracle_lib, shape):
+    """Scales 2^-20 .. 2^20 (term exponents spread over 80 binades, beyond
+    float64): every output against the exact rational sum, rounded to the
+    nearest fp16 (ties to even) by exact comparison with the fp16 values
+    around it."""
+    from fractions import Fraction
+    M, N, K = shape
+    A, B, SA, SB = workloads.make_mx_inputs([M], [N], [K], 10, dist="wide")
+    a = ind.unpack_fp4(A[0], M, K)
+    b = ind.unpack_fp4(B[0], N, K)
+    C = oracle_lib.mx_group_gemm([M], [N], [K], A, B, SA, SB)[0]
+    for m in range(M):
+        for n in range(N):
+            x = ind.exact_mx_element(a[m], SA[0][m], b[n], SB[0][n])
+            got = float(C[m, n])
+            cand = np.float16(float(x))
+            near = sorted({float(v) for v in (cand, np.nextafter(cand, np.float16(-np.inf)),
+                                              np.nextafter(cand, np.float16(np.inf))) if np.isfinite(v)},
+                          key=lambda v: abs(Fraction(v) - x))
+            best = near[0]
+            if len(near) > 1 and abs(Fraction(near[1]) - x) == abs(Fraction(near[0]) - x):
+                best = [v for v in near[:2] if (int(np.float16(v).view(np.uint16)) & 1) == 0][0]
+            if x == 0:
+                assert got == 0.0
+            elif abs(x) >= 65520:
+                assert np.isinf(got) and (got > 0) == (x > 0)
+            else:
+                assert got == best, (m, n, float(x), got, best)
+
+
+def test_mx_onehot_block_index(oracle_lib):
+    """A single non-zero code at K index k in A and in B, with a distinct
+    scale per 32-K block: the one output is e2m1 * e2m1 * 2^(ea + eb - 254)
+    with the scales of block k // 32 (block edges 31, 32, 63, 64)."""
+    M, N, K = 2, 3, 128
+    table = ind.e2m1_table()
+    sa = np.array([[120, 125, 130, 135]] * M, dtype=np.uint8)
+    sb = np.array([[131, 126, 121, 129]] * N, dtype=np.uint8)
+    for k in (0, 1, 31, 32, 63, 64, 127):
+        a = np.zeros((M, K), np.uint8)
+        b = np.zeros((N, K), np.uint8)
+        a[1, k] = 3      # 1.5
+        b[2, k] = 13     # -3
+        C, X = oracle_lib.mx_group_gemm([M], [N], [K], [ind.pack_fp4(a)], [ind.pack_fp4(b)], [sa], [sb], exact=True)
+        want = table[3] * table[13] * 2.0 ** (int(sa[1, k // 32]) + int(sb[2, k // 32]) - 254)
+        assert X[0][1, 2] == want, k
+        assert np.count_nonzero(X[0]) == 1
+
+
+def test_mx_unit_scales_equal_nvfp4_unit_scales(oracle_lib):
+    """With every scale 1.0 the two formats compute the same sum of E2M1
+    products: the MX oracle equals the (separately pinned) NVFP4 oracle."""
+    M, N, K = [5, 9], [7, 3], [256, 96]
+    A, B, _, _ = workloads.make_mx_inputs(M, N, K, 4)
+    nsa = [np.full((m, k // 16), 0x38, np.uint8) for m, k in zip(M, K)]
+    nsb = [np.full((n, k // 16), 0x38, np.uint8) for n, k in zip(N, K)]
+    msa = [np.full((m, k // 32), 127, np.uint8) for m, k in zip(M, K)]
+    msb = [np.full((n, k // 32), 127, np.uint8) for n, k in zip(N, K)]
+    Cn = oracle_lib.group_gemm(M, N, K, A, B, nsa, nsb)
+    Cm = oracle_lib.mx_group_gemm(M, N, K, A, B, msa, msb)
+    for a, b in zip(Cn, Cm):
+        np.testing.assert_array_equal(a.view(np.uint16), b.view(np.uint16))
+
+
+def test_mx_exponent_spread_limit(oracle_lib):
+    """Scales 2^-67 and 2^+23 in one dot product (a 90-binade spread): the
+    oracle's integer sum matches an exact rational computation; a spread
+    beyond 96 binades is reported, not approximated."""
+    K = 64
+    rng = np.random.default_rng(3)
+    a = rng.integers(0, 16, size=(1, K), dtype=np.uint8)
+    b = rng.integers(0, 16, size=(1, K), dtype=np.uint8)
+    sb = np.array([[127, 127]], np.uint8)
+    sa = np.array([[60, 150]], np.uint8)
+    c16, x = oracle_lib.mx_gemm_element(1, 1, K, ind.pack_fp4(a), ind.pack_fp4(b), sa, sb, 0, 0)
+    want = ind.exact_mx_element(a[0], sa[0], b[0], sb[0])
+    assert x == float(want)
+    assert c16 == int(np.float16(float(want)).view(np.uint16))
+    with pytest.raises(ValueError):
+        oracle_lib.mx_gemm_element(1, 1, K, ind.pack_fp4(a), ind.pack_fp4(b), np.array([[20, 150]], np.uint8),
+                                   sb, 0, 0)
+
+
+def test_mx_pins_detect_plausible_mistakes(oracle_lib):
+    """A scale per 16 K instead of 32, or a missing -127 bias, changes the
+    brute-force values the MX pins compare against."""
+    M, N, K = 4, 4, 128
+    A, B, SA, SB = workloads.make_mx_inputs([M], [N], [K], 12)
+    _, base = ind.brute_mx_group(A[0], B[0], SA[0], SB[0], M, N, K)
+    sa16 = np.repeat(SA[0], 2, axis=1)[:, : K // 32]       # block k//16 read as k//32
+    assert not np.array_equal(ind.brute_mx_group(A[0], B[0], sa16, SB[0], M, N, K)[1], base)
+    C = oracle_lib.mx_group_gemm([M], [N], [K], A, B, SA, SB, exact=True)[1][0]
+    assert not np.array_equal(C * 2.0, base)
+    np.testing.assert_array_equal(C, base)

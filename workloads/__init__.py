@@ -18,6 +18,10 @@ stated for them):
     scale is a positive normal E4M3 value in [0.125, 15].
   * Other scale distributions for edge tests: "unit" (every scale 1.0, code
     0x38), "finite" (any non-NaN E4M3 code, signs and subnormals included).
+  * MXFP4 form: the same A, B bytes; E8M0 scales (one per 32 K) with the
+    exponent uniform over {-3..3} (codes 124..130), the range of the NVFP4
+    scales' exponents; "unit" (code 127) and "wide" (codes 107..147, a
+    product spread up to 2^80) for edge tests.
 """
 from __future__ import annotations
 
@@ -125,11 +129,42 @@ def config_inputs(cfg: dict, variant: int = 0):
     return make_inputs(cfg["M"], cfg["N"], cfg["K"], cfg["seed"], variant=variant)
 
 
-def algorithmic_bytes(M, N, K) -> int:
-    """Bytes each input is read once plus C written once (fp16)."""
+def mx_scale_codes(key: np.uint64, count: int, dist: str = "pos") -> np.ndarray:
+    """E8M0 scale codes: "pos" 124..130, "unit" 127, "wide" 107..147."""
+    d = draws(key, count)
+    if dist == "pos":
+        return ((d >> np.uint64(32)) % np.uint64(7) + np.uint64(124)).astype(np.uint8)
+    if dist == "unit":
+        return np.full(count, 127, dtype=np.uint8)
+    if dist == "wide":
+        return ((d >> np.uint64(32)) % np.uint64(41) + np.uint64(107)).astype(np.uint8)
+    raise ValueError("unknown E8M0 scale distribution %r" % dist)
+
+
+_T_MXSFA, _T_MXSFB = 5, 6
+
+
+def make_mx_inputs(M, N, K, seed: int, *, dist: str = "pos", variant: int = 0):
+    """MXFP4 inputs: the A, B bytes of make_inputs and E8M0 scales,
+    SFA (M, K/32), SFB (N, K/32)."""
+    A, B, SA, SB = [], [], [], []
+    for gi, (m, n, k) in enumerate(zip(M, N, K)):
+        if k % 32:
+            raise ValueError("K must be a multiple of 32")
+        a, b, _, _ = make_group(seed, gi, m, n, k, variant=variant)
+        A.append(a)
+        B.append(b)
+        SA.append(mx_scale_codes(stream_key(seed, variant, gi, _T_MXSFA), m * k // 32, dist).reshape(m, k // 32))
+        SB.append(mx_scale_codes(stream_key(seed, variant, gi, _T_MXSFB), n * k // 32, dist).reshape(n, k // 32))
+    return A, B, SA, SB
+
+
+def algorithmic_bytes(M, N, K, scale_block: int = 16) -> int:
+    """Bytes each input is read once plus C written once (fp16); one scale
+    byte per scale_block K of a row (16 for NVFP4, 32 for MXFP4)."""
     tot = 0
     for m, n, k in zip(M, N, K):
-        tot += m * k // 2 + n * k // 2 + m * k // 16 + n * k // 16 + 2 * m * n
+        tot += m * k // 2 + n * k // 2 + m * k // scale_block + n * k // scale_block + 2 * m * n
     return tot
 
 
