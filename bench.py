@@ -43,6 +43,8 @@ METRIC = "µs/call + achieved HBM GB/s & TFLOP/s, NVFP4 grouped GEMM g=8 K=7168 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 KERNEL = "nvfp4_group_gemm_kernel"
+MX_KERNEL = "mxfp4_group_gemm_kernel"
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 CALIB_KERNEL = "neg"            # torch.neg's elementwise kernel: reads and writes the copy size
 CSRC = os.path.join(ROOT, "nvfp4_block_scaled_grouped_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -57,6 +59,9 @@ def parse():
                     help="workload name (default: the g=8 K=7168 N=4096 grouped GEMM)")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated through (0: enough to exceed 384 MB, at most 64)")
+    ap.add_argument("--format", choices=("nvfp4", "mxfp4"), default="nvfp4",
+                    help="nvfp4 (E4M3 scale per 16 K, the headline) or mxfp4 (E8M0 scale per 32 K, "
+                         "mxfp4_group_gemm on the block-scaled FP4 MFMA)")
     ap.add_argument("--sf-layout", choices=("row-major", "blocked"), default="row-major",
                     help="scale layout: row-major (nvfp4_group_gemm) or the blocked 128 x 4 atom "
                          "layout (nvfp4_group_gemm_blocked)")
@@ -81,14 +86,14 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def traffic_file(workload: str) -> str:
-    return os.path.join(PROFILES, "%s_%s_traffic.txt" % (KERNEL, workload))
+def traffic_file(workload: str, kernel: str = KERNEL) -> str:
+    return os.path.join(PROFILES, "%s_%s_traffic.txt" % (kernel, workload))
 
 
-def read_traffic(workload: str):
+def read_traffic(workload: str, kernel: str = KERNEL):
     """Bytes per launch from the stored counter summary, or None when there
     is none or it was taken on other kernel sources."""
-    path = traffic_file(workload)
+    path = traffic_file(workload, kernel)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -114,12 +119,12 @@ def counter_means(path: str):
     return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
 
 
-def traffic_from(fetch_csv: str, write_csv: str, copy_mb: int):
+def traffic_from(fetch_csv: str, write_csv: str, copy_mb: int, kernel: str = KERNEL):
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         means = counter_means(path)
-        gemm = [v for k, v in means.items() if KERNEL in k]
-        calib = [v for k, v in means.items() if CALIB_KERNEL in k and KERNEL not in k]
+        gemm = [v for k, v in means.items() if kernel in k]
+        calib = [v for k, v in means.items() if CALIB_KERNEL in k and kernel not in k]
         if len(gemm) != 1 or len(calib) != 1:
             raise SystemExit("%s: expected one GEMM and one copy kernel, found %s" % (path, list(means)))
         known_kib = copy_mb * 1024.0
@@ -129,13 +134,16 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mb: int):
     return out
 
 
-def make_device_sets(cfg, nsets, torch, blocked=False, blocked_bytes=None):
+def make_device_sets(cfg, nsets, torch, blocked=False, blocked_bytes=None, fmt="nvfp4"):
     """Device copies of nsets input sets.  With blocked scales, each scale
     array is a fresh draw of scale codes of the blocked array's size (the
     timing does not depend on which valid scale sits where)."""
     sets = []
     for v in range(nsets):
-        A, B, SA, SB = workloads.config_inputs(cfg, variant=v)
+        if fmt == "mxfp4":
+            A, B, SA, SB = workloads.make_mx_inputs(cfg["M"], cfg["N"], cfg["K"], cfg["seed"], variant=v)
+        else:
+            A, B, SA, SB = workloads.config_inputs(cfg, variant=v)
         if blocked:
             kk = cfg["K"]
             SA = [workloads.scale_codes(workloads.stream_key(cfg["seed"], v, i, 101), blocked_bytes(m, k))
@@ -150,7 +158,7 @@ def make_device_sets(cfg, nsets, torch, blocked=False, blocked_bytes=None):
     return sets
 
 
-def cpu_baseline(cfg, target_s):
+def cpu_baseline(cfg, target_s, fmt="nvfp4"):
     """The oracle, as it is, on the first r_i rows of every group (all N_i
     columns, all K_i), r_i the same fraction of M_i in each group, grown until
     the run takes about target_s; scaled to the whole workload by
@@ -159,7 +167,13 @@ def cpu_baseline(cfg, target_s):
     oracle.build(force=False)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     g = len(M)
-    inputs = [workloads.make_group(cfg["seed"], i, M[i], N[i], K[i]) for i in range(g)]
+    if fmt == "mxfp4":
+        mx = workloads.make_mx_inputs(M, N, K, cfg["seed"])
+        inputs = [tuple(x[i] for x in mx) for i in range(g)]
+        run_oracle = oracle.mx_group_gemm
+    else:
+        inputs = [workloads.make_group(cfg["seed"], i, M[i], N[i], K[i]) for i in range(g)]
+        run_oracle = oracle.group_gemm
     total_macs = sum(m * n * k for m, n, k in zip(M, N, K))
     threads = oracle.max_threads()
 
@@ -168,8 +182,7 @@ def cpu_baseline(cfg, target_s):
         A = [inputs[i][0][:rows[i]] for i in range(g)]
         SA = [inputs[i][2][:rows[i]] for i in range(g)]
         t0 = time.perf_counter()
-        oracle.group_gemm(rows, N, K, A, [x[1] for x in inputs], SA, [x[3] for x in inputs],
-                          nthreads=threads)
+        run_oracle(rows, N, K, A, [x[1] for x in inputs], SA, [x[3] for x in inputs], nthreads=threads)
         return rows, time.perf_counter() - t0
 
     frac = min(1.0, threads / max(1.0, sum(M)))
@@ -191,7 +204,8 @@ def main():
     args = parse()
     if args.traffic_from:
         mb = args.calib_copy_mb or 512
-        t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb)
+        t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb,
+                         MX_KERNEL if args.format == "mxfp4" else KERNEL)
         total = int(round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]))
         print(json.dumps({"source_sha256": source_digest(), "calib_copy_mb": mb, "counters": t,
                           "traffic_bytes_per_launch": total}, indent=1))
@@ -207,16 +221,21 @@ def main():
     nv.load()
     cfg = next(c for c in workloads.CONFIGS if c["name"] == args.config)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    abytes = workloads.algorithmic_bytes(M, N, K)
+    mx = args.format == "mxfp4"
+    if mx and args.sf_layout == "blocked":
+        print("bench.py: the MXFP4 entry point takes row-major scales only", file=sys.stderr)
+        sys.exit(2)
+    abytes = workloads.algorithmic_bytes(M, N, K, 32 if mx else 16)
     flops = workloads.algorithmic_flops(M, N, K)
     nsets = args.sets or min(64, max(1, -(-384 * 2 ** 20 // abytes)))
     blocked = args.sf_layout == "blocked"
-    sets = make_device_sets(cfg, nsets, torch, blocked, nv.blocked_scale_bytes)
+    sets = make_device_sets(cfg, nsets, torch, blocked, nv.blocked_scale_bytes, args.format)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     calls = [nv.GroupGemmCall(M, N, K, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
                               [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
-                              [t.data_ptr() for t in s["C"]], sh, blocked=blocked) for s in sets]
+                              [t.data_ptr() for t in s["C"]], sh, blocked=blocked, fmt=args.format)
+             for s in sets]
 
     def step(i):
         rc = calls[i % nsets]()
@@ -249,7 +268,8 @@ def main():
 
     gbps = abytes / us / 1e3
     tflops = flops / us / 1e6
-    traffic = read_traffic(cfg["name"] + ("_blocked_sf" if blocked else ""))
+    traffic = read_traffic(cfg["name"] + ("_blocked_sf" if blocked else "") + ("_mxfp4" if mx else ""),
+                           MX_KERNEL if mx else KERNEL)
     out = {
         "metric": METRIC,
         "value": round(us, 3),
@@ -276,8 +296,19 @@ def main():
                      "hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": abytes}},
     }
+    if mx:
+        # The FP4 MFMA floor (5.95 us at g8 K7168 N4096) lies far below the
+        # HBM one: this form is bound by HBM.
+        out["config"]["format"] = "mxfp4"
+        out["roofline"] = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                           "algorithmic_bytes": abytes,
+                           "mfma": {"achieved": round(tflops, 1), "peak": FP4_MFMA_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4)}}
+        out["dtype"] = "fp4"
+        out["metric"] = METRIC.replace("NVFP4", "MXFP4")
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.format)
     print(json.dumps(out), flush=True)
 
 
