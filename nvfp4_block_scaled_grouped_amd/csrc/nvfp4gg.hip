@@ -87,8 +87,10 @@ constexpr uint32_t kNoSlot = 0xF0000000u;
 #ifndef NVFP4_INTERLEAVE
 #define NVFP4_INTERLEAVE 1
 #endif
-#ifndef NVFP4_RING3
-#define NVFP4_RING3 1
+// Register ring depth (stages of B and A loads in flight) of tiles of up to
+// 4 fragments (2 or 4; larger tiles use 2, for lack of registers).
+#ifndef NVFP4_RING_SMALL
+#define NVFP4_RING_SMALL 2
 #endif
 #ifndef NVFP4_XCD_REMAP
 #define NVFP4_XCD_REMAP 1
@@ -352,6 +354,28 @@ __device__ __forceinline__ h2_t scales2(uint32_t sc, uint32_t shift)
     return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc >> shift, 1.0f, false);
 }
 
+// Stages J .. L-1 of an unrolled pass: f(slot J % R, phase J % 4, i + J),
+// all of them, or (the tail) those below n.
+template <int J, int L, int R, class F>
+__device__ __forceinline__ void phase_pass(F& f, int i)
+{
+    if constexpr (J < L) {
+        f(Parity<J % R>{}, Parity<J % 4>{}, i + J);
+        phase_pass<J + 1, L, R>(f, i);
+    }
+}
+
+template <int J, int L, int R, class F>
+__device__ __forceinline__ void phase_tail(F& f, int i, int n)
+{
+    if constexpr (J < L) {
+        if (i + J < n) {
+            f(Parity<J % R>{}, Parity<J % 4>{}, i + J);
+            phase_tail<J + 1, L, R>(f, i, n);
+        }
+    }
+}
+
 // The end of a segment: chains of one segment meet in the scratch slot; the
 // last chain finishes the tile alone, or as one of several contributors
 // (partial-tile store, counter, and the fix-up by the last to arrive).
@@ -521,7 +545,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
 //     buffer, one piece per k-step of the MFMA loop, then re-loaded with
 //     stage i + 1 + kRing.
 //   * One LDS-only barrier ends the stage.
-template <int MF>
+template <int MF, bool kBlocked>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
                                             bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
@@ -543,7 +567,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
     // Blocked scales: rows padded to a multiple of 128 (the layout's atoms
     // are 128 rows x 4 scales; K / 16 is a multiple of 8 here).
-    const bool blocked = args.blocked_sf != 0;
+    constexpr bool blocked = kBlocked;
     const uint32_t sf_rows_a = blocked ? (uint32_t)(M + 127) & ~127u : (uint32_t)M;
     const uint32_t sf_rows_b = blocked ? (uint32_t)(N + 127) & ~127u : (uint32_t)N;
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, sf_rows_a * row_scales);
@@ -565,8 +589,8 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     // area.
     constexpr int kU = NA > kWaves ? 2 : 1;
     // Register ring depth: stage i's loads go out kRing stages ahead.
-    constexpr int kRing = NVFP4_RING3 && MF <= 4 ? 3 : 2;
-    static_assert(kRing == 2 || kRing == 3, "ring of two or three stages");
+    constexpr int kRing = MF <= 4 ? NVFP4_RING_SMALL : 2;
+    static_assert(kRing == 2 || kRing == 4, "the ring depth divides the 4-stage scale block");
     uint32_t offA[2];
     h8_t* adst[2];          // k-step 0 of the unit's fragment in LDS buffer 0
     uint32_t abuf_step[2];  // bytes from buffer 0 to buffer 1 (0 for the discard area)
@@ -689,8 +713,14 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             for (int f = 0; f < 2; ++f) acc[i][f] = zero_acc();
         lds_barrier();
 
-        auto stage = [&](auto parity, int i) {
+        // Stage i of the chain, at ring slot p = i % kRing and scale-block
+        // phase q = i % 4, both known at compile time (the loop below is
+        // unrolled by 4), so the stage has no branch: a branch here would
+        // make the compiler's wait counts at its join conservative, which
+        // drains the load ring.
+        auto stage = [&](auto parity, auto phase, int i) {
             constexpr int p = decltype(parity)::value;
+            constexpr int q = decltype(phase)::value;
             const uint32_t sb2 = sbyte(i + kRing);
             const uint32_t sb3 = sbyte(i + 1 + kRing);
             // LDS A buffers: this stage reads buffer i % 2 and writes the other.
@@ -710,8 +740,10 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             h2_t saf[2];
 #pragma unroll
             for (int x = 0; x < kU; ++x) saf[x] = scales2(scale_a(ia, x), sshift);
-            if ((i & 3) == 0 && i + 4 < n) scale_load(i + 4);
-            if ((i & 3) == 2 && i + 2 < n) scale_store(((i >> 2) + 1) & 1);
+            // Past the chain's end these read bytes never used (zeros past
+            // the buffer) and fill a staging buffer nobody reads.
+            if constexpr (q == 0) scale_load(i + 4);
+            if constexpr (q == 2) scale_store(((i >> 2) + 1) & 1);
 
             // k-step pipeline: the B dequant of k-step v + 1 is issued before
             // the MFMAs of k-step v; the scheduling barrier at the end of each
@@ -771,13 +803,8 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         };
 
         int i = 0;
-        for (; i + kRing - 1 < n; i += kRing) {
-            stage(Parity<0>{}, i);
-            stage(Parity<1>{}, i + 1);
-            if constexpr (kRing > 2) stage(Parity<2>{}, i + 2);
-        }
-        if (i < n) stage(Parity<0>{}, i);
-        if (kRing > 2 && i + 1 < n) stage(Parity<1>{}, i + 1);
+        for (; i + 3 < n; i += 4) phase_pass<0, 4, kRing>(stage, i);
+        phase_tail<0, 4, kRing>(stage, i, n);
     }
     finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
@@ -846,9 +873,11 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
 {
     constexpr int NA = 2 * MF;
     constexpr int kU = NA > kWaves ? 2 : 1;
-    // Stages of B in flight: the MFMAs take a fraction of what the B
-    // stream does, so the ring is as deep as the registers allow.
-    constexpr int kRing = MF <= 2 ? 8 : MF <= 4 ? 6 : 3;
+    // Stages of B in flight.  Measured on MI355X: 4 beats 8 (whose first
+    // burst of loads delays every workgroup's first stage by several us)
+    // on every workload; depths of 6 and 3 compiled to loops whose wait
+    // counts drained the ring every pass.
+    constexpr int kRing = 4;
     // A fragments read from LDS per group (the scheduling barrier between
     // groups keeps the compiler from loading every fragment of the stage up
     // front, which large tiles have no registers for).
@@ -973,6 +1002,20 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
             // reloads: B of stage i + kRing, A of stage i + 1 + kRing.
 #pragma unroll
             for (int x = 0; x < kU; ++x) put_a(lb ^ 1, x, aq[p][x], as[p][x]);
+            // The slot's old values are consumed before its reloads are
+            // issued, so the reloads can take the same registers (otherwise
+            // the compiler copies ring values whose loads are in flight and
+            // waits for them).
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                fence_after(bq[p][f]);
+                fence_after(bs[p][f]);
+            }
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                fence_after(aq[p][x]);
+                fence_after(as[p][x]);
+            }
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
                 bq[p][f] = load16(rB, offB[f], sbyte(i + kRing));
@@ -1019,7 +1062,7 @@ __device__ __forceinline__ Pos uniform(const Pos& p)
 // The persistent walk of one workgroup over its cost range: every segment
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
-template <bool kMx>
+template <bool kMx, bool kBlocked>
 __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
     const int w = uniform(worker_id(args.G));
@@ -1046,12 +1089,12 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
                 }
             } else {
                 switch (pos.frags) {
-                    case 1: run_segment<1>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 2: run_segment<2>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 3: run_segment<3>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 4: run_segment<4>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 5: run_segment<5>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    default: run_segment<6>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 1: run_segment<1, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 2: run_segment<2, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 3: run_segment<3, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 4: run_segment<4, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 5: run_segment<5, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    default: run_segment<6, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
                 }
             }
         }
@@ -1064,14 +1107,22 @@ __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const Launch
 {
     __shared__ SharedMem sm;
     __shared__ int s_flag;
-    walk_range<false>(args, sm, &s_flag);
+    walk_range<false, false>(args, sm, &s_flag);
+}
+
+// NVFP4 with the scales in the blocked layout.
+__global__ __launch_bounds__(kThreads) void nvfp4_blocked_sf_gemm_kernel(const LaunchArgs args)
+{
+    __shared__ SharedMem sm;
+    __shared__ int s_flag;
+    walk_range<false, true>(args, sm, &s_flag);
 }
 
 __global__ __launch_bounds__(kThreads) void mxfp4_group_gemm_kernel(const LaunchArgs args)
 {
     __shared__ SharedMem sm;
     __shared__ int s_flag;
-    walk_range<true>(args, sm, &s_flag);
+    walk_range<true, false>(args, sm, &s_flag);
 }
 
 // Writes zeros to C of a group with K == 0 (the empty sum).
@@ -1295,6 +1346,8 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         args.counters = ws.counters;
         if (fmt == kFmtMxfp4)
             hipLaunchKernelGGL(mxfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
+        else if (blocked_sf)
+            hipLaunchKernelGGL(nvfp4_blocked_sf_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
         else
             hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
         const hipError_t e = hipGetLastError();

@@ -85,11 +85,11 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
 // about 50 ns.  NVFP4: measured MI355X stage times 1.2, 1.45, 1.75, 2.3 and
-// 2.8 us for 2 to 6 fragments, one fragment extrapolated.  MXFP4: stage
-// times of its kernel (about 0.5 to 0.8 us).
+// 2.8 us for 2 to 6 fragments, one fragment extrapolated.  MXFP4: measured
+// 1.15, 1.25, 1.3 and 1.8 us for 2, 3, 4 and 5-6 fragments.
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    if (fmt == kFmtMxfp4) return f <= 2 ? 10 : f <= 4 ? 12 : 15;
+    if (fmt == kFmtMxfp4) return f <= 1 ? 22 : f == 2 ? 23 : f == 3 ? 25 : f == 4 ? 26 : 36;
     return f <= 1 ? 21 : f == 2 ? 24 : f == 3 ? 29 : f == 4 ? 35 : f == 5 ? 46 : kMaxUnitCost;
 }
 
