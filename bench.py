@@ -44,6 +44,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 KERNEL = "nvfp4_group_gemm_kernel"
 MX_KERNEL = "mxfp4_group_gemm_kernel"
+BLOCKED_KERNEL = "nvfp4_blocked_sf_gemm_kernel"
 FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 CALIB_KERNEL = "neg"            # torch.neg's elementwise kernel: reads and writes the copy size
 CSRC = os.path.join(ROOT, "nvfp4_block_scaled_grouped_amd", "csrc")
@@ -73,6 +74,13 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the counter-derived traffic per launch and exit (no GPU use)")
     return ap.parse_args()
+
+
+def kernel_name(args) -> str:
+    """The GEMM kernel a run launches."""
+    if args.format == "mxfp4":
+        return MX_KERNEL
+    return BLOCKED_KERNEL if args.sf_layout == "blocked" else KERNEL
 
 
 def source_digest() -> str:
@@ -204,8 +212,7 @@ def main():
     args = parse()
     if args.traffic_from:
         mb = args.calib_copy_mb or 512
-        t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb,
-                         MX_KERNEL if args.format == "mxfp4" else KERNEL)
+        t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb, kernel_name(args))
         total = int(round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]))
         print(json.dumps({"source_sha256": source_digest(), "calib_copy_mb": mb, "counters": t,
                           "traffic_bytes_per_launch": total}, indent=1))
@@ -268,8 +275,7 @@ def main():
 
     gbps = abytes / us / 1e3
     tflops = flops / us / 1e6
-    traffic = read_traffic(cfg["name"] + ("_blocked_sf" if blocked else "") + ("_mxfp4" if mx else ""),
-                           MX_KERNEL if mx else KERNEL)
+    traffic = read_traffic(cfg["name"], kernel_name(args))
     out = {
         "metric": METRIC,
         "value": round(us, 3),
