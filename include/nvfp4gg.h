@@ -127,11 +127,20 @@ int mxfp4_group_gemm(int g, const int* M, const int* N, const int* K,
 int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
                       void* out, void* stream);
 
+/* Bound, in polls of about a microsecond, on how long the workgroup that
+ * finishes a tile split over several workgroups waits for the others
+ * (process-wide; default 2^20).  When all workgroups of a launch run at once,
+ * as on an otherwise idle GPU, the wait ends long before.  When it runs out,
+ * the tile is finished by the last of the others instead, so results do not
+ * depend on it; 0 makes that the rule (the test of that path uses it).
+ * Returns NVFP4GG_INVALID_ARG for a negative count. */
+int nvfp4_group_gemm_set_wait_limit(int polls);
+
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 3 (2 added nvfp4_group_gemm_blocked, 3
- * mxfp4_group_gemm). */
+/* ABI version of this header: 4 (2 added nvfp4_group_gemm_blocked, 3
+ * mxfp4_group_gemm, 4 nvfp4_group_gemm_set_wait_limit). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

@@ -39,6 +39,8 @@ def load():
     lib.nvfp4_dequant_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.nvfp4_dequant_f16.restype = ctypes.c_int
+    lib.nvfp4_group_gemm_set_wait_limit.argtypes = [ctypes.c_int]
+    lib.nvfp4_group_gemm_set_wait_limit.restype = ctypes.c_int
     lib.nvfp4_group_gemm_last_error.argtypes = []
     lib.nvfp4_group_gemm_last_error.restype = ctypes.c_char_p
     lib.nvfp4_group_gemm_version.argtypes = []
@@ -180,6 +182,12 @@ def dequant_f16(X, SFX, out, rows: int, K: int, stream=None):
     _check(lib.nvfp4_dequant_f16(int(rows), int(K), _ptr(X, "X", _BYTES), _ptr(SFX, "SFX", _BYTES),
                                  _ptr(out, "out", ("float16",)), ctypes.c_void_p(_stream_handle(stream))))
     return out
+
+
+def set_wait_limit(polls: int):
+    """Bound on a split tile's finisher waiting for the other contributors
+    (see include/nvfp4gg.h); 0 hands every fix-up to the last arriver."""
+    _check(load().nvfp4_group_gemm_set_wait_limit(int(polls)))
 
 
 def version() -> int:

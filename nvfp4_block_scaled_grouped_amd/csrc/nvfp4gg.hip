@@ -50,6 +50,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -81,6 +82,14 @@ constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lg
 // A partial-slot offset past the end of every workspace (the host checks
 // that the workspace stays below it): buffer loads there return zeros.
 constexpr uint32_t kNoSlot = 0xF0000000u;
+// Split-tile counter: arrivals of the contributors after the first in the
+// low bits, the first contributor's claim of the fix-up, or its hand-over.
+constexpr int kCountMask = 0xFFFF;
+constexpr int kClaim = 1 << 16;
+constexpr int kHandOver = 1 << 17;
+// Default bound on the first contributor's wait (polls of about a
+// microsecond each).
+constexpr int kWaitLimit = 1 << 20;
 
 // Issue-order hints that interleave the B dequantisation with the MFMAs of
 // each k-step (0 leaves the order to the compiler).
@@ -119,6 +128,7 @@ struct LaunchArgs {
     int G;                // workgroups
     int ngroups;
     int blocked_sf;       // scales in the blocked (128 x 4 atom) layout, else row-major
+    int wait_limit;       // polls of a tile's first contributor waiting for the others
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
@@ -424,18 +434,60 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     auto slot_base = [&](int w) {
         return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + ewave_in_slot;
     };
-    store_block<MF>(rP, slot_base(me), acc);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old =
-            __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = (old == w_last - w_first) ? 1 : 0;
+    // Who finishes the tile.  The first contributor's range ends with the
+    // tile's first stages and carries the tile's start-up and wind-down cost
+    // (kTileCost), so it should: it claims the fix-up and waits for the
+    // others, a bounded number of polls (all workgroups of the grid run at
+    // once when it fits the chip, so the others are running and never wait
+    // themselves).  The others store their partials and count themselves in.
+    // If the wait runs out, the first contributor stores its partial too and
+    // swaps its claim for a hand-over, and whoever then completes the count
+    // finishes the tile: exactly one workgroup does, and nobody waits
+    // unboundedly.
+    const int others = w_last - w_first;
+    bool fix;
+    if (me != w_first) {
+        store_block<MF>(rP, slot_base(me), acc);
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const int old =
+                __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_flag = ((old & kCountMask) + 1 == others && (old & kHandOver)) ? 1 : 0;
+        }
+        __syncthreads();
+        fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+        __syncthreads();   // s_flag is reused below and by the next segment
+    } else {
+        if (threadIdx.x == 0) {
+            const int old =
+                __hip_atomic_fetch_add(args.counters + tile, kClaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            int done = (old & kCountMask) == others;
+            for (int poll = 0; !done && poll < args.wait_limit; ++poll) {
+                __builtin_amdgcn_s_sleep(2);
+                done = (__hip_atomic_load(args.counters + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                        kCountMask) == others;
+            }
+            *s_flag = done;
+        }
+        __syncthreads();
+        fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+        __syncthreads();
+        if (!fix) {
+            store_block<MF>(rP, slot_base(me), acc);
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int old = __hip_atomic_fetch_add(args.counters + tile, kHandOver - kClaim, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+                *s_flag = (old & kCountMask) == others;   // the count completed meanwhile: still ours
+            }
+            __syncthreads();
+            fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    const bool last = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
-    __syncthreads();   // s_flag is reused by the next segment
-    if (!last) return;
+    if (!fix) return;
     // Sum the contributors' partials in workgroup order, so the result does
     // not depend on who arrived last.  Loads carry the device-scope
     // coherence bit; a contributor index past w_last gets an offset beyond
@@ -1173,7 +1225,6 @@ int fail(int code, const std::string& msg)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Workspace of the split-tile fixup, one per (device, stream): three
 // partial-tile slots per workgroup and the per-tile counters (zero between calls; the last contributor
@@ -1225,6 +1276,9 @@ int get_workspace(int dev, hipStream_t s, int G, int tiles, Workspace& out)
     return NVFP4GG_OK;
 }
 
+// Bound on a first contributor's wait (see finish_segment), process-wide.
+std::atomic<int> g_wait_limit{kWaitLimit};
+
 int device_cus(int dev)
 {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -1240,7 +1294,14 @@ int device_cus(int dev)
 
 extern "C" const char* nvfp4_group_gemm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int nvfp4_group_gemm_version(void) { return 3; }
+extern "C" int nvfp4_group_gemm_version(void) { return 4; }
+
+extern "C" int nvfp4_group_gemm_set_wait_limit(int polls)
+{
+    if (polls < 0) return fail(NVFP4GG_INVALID_ARG, "the wait limit must be >= 0");
+    g_wait_limit.store(polls);
+    return NVFP4GG_OK;
+}
 
 namespace {
 
@@ -1344,15 +1405,14 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         if (rc != NVFP4GG_OK) return rc;
         args.partials = ws.partials;
         args.counters = ws.counters;
-        if (fmt == kFmtMxfp4)
-            hipLaunchKernelGGL(mxfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
-        else if (blocked_sf)
-            hipLaunchKernelGGL(nvfp4_blocked_sf_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
-        else
-            hipLaunchKernelGGL(nvfp4_group_gemm_kernel, dim3(args.G), dim3(kThreads), 0, s, args);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        const void* kernel = fmt == kFmtMxfp4 ? reinterpret_cast<const void*>(&mxfp4_group_gemm_kernel)
+                             : blocked_sf     ? reinterpret_cast<const void*>(&nvfp4_blocked_sf_gemm_kernel)
+                                              : reinterpret_cast<const void*>(&nvfp4_group_gemm_kernel);
+        args.wait_limit = g_wait_limit.load();
+        void* kargs[] = {&args};
+        const hipError_t le = hipLaunchKernel(kernel, dim3(args.G), dim3(kThreads), kargs, 0, s);
+        if (le != hipSuccess)
+            return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(le));
     }
     return NVFP4GG_OK;
 }

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert nv.version() == 3
+    assert nv.version() == 4
 
 
 A16 = 0x10000          # fake, aligned addresses: never dereferenced, every case
@@ -135,3 +135,8 @@ def test_mxfp4_entry_validates(lib):
     assert rc == nv.UNSUPPORTED and "K % 128" in nv.last_error()
     rc = nv.group_gemm_ptrs([8], [8], [256], [MIS], [A16], [A16], [A16], [A16], 0, fmt="mxfp4")
     assert rc == nv.INVALID_ARG
+
+
+def test_wait_limit_validation(lib):
+    assert lib.nvfp4_group_gemm_set_wait_limit(-1) == nv.INVALID_ARG
+    assert lib.nvfp4_group_gemm_set_wait_limit(1 << 20) == nv.OK

@@ -216,3 +216,29 @@ def test_long_segments_run_as_several_chains(nv, oracle_lib):
         r.append(np.uint16(c16).view(np.float16))
         x.append(ex)
     _compare.assert_close(np.array(y), np.array(r), np.array(x), "long segments")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_fixup_hand_over_path(nv, oracle_lib, fmt):
+    """With a wait limit of 0, the first contributor of every split tile
+    hands the fix-up over to the last of the others (the path taken when a
+    wait runs out).  Shapes whose tiles are split over 2 to 7 workgroups."""
+    M, N, K = [192, 320], [3072, 1024], [4096, 2048]
+    _say("hand-over fix-up %s M=%s N=%s K=%s" % (fmt, M, N, K))
+    if fmt == "mxfp4":
+        A, B, SA, SB = workloads.make_mx_inputs(M, N, K, 71)
+        C_ref, X = oracle_lib.mx_group_gemm(M, N, K, A, B, SA, SB, exact=True)
+    else:
+        A, B, SA, SB = workloads.make_inputs(M, N, K, 71)
+        C_ref, X = oracle_lib.group_gemm(M, N, K, A, B, SA, SB, exact=True)
+    dC = [torch.full((m, n), 0, dtype=torch.int16, device="cuda").fill_(SENTINEL).view(torch.float16)
+          for m, n in zip(M, N)]
+    nv.set_wait_limit(0)
+    try:
+        nv.group_gemm([_dev(a) for a in A], [_dev(b) for b in B], [_dev(s) for s in SA], [_dev(s) for s in SB],
+                      dC, M=M, N=N, K=K, fmt=fmt)
+        torch.cuda.synchronize()
+    finally:
+        nv.set_wait_limit(1 << 20)
+    for i in range(len(M)):
+        _compare.assert_close(dC[i].cpu().numpy(), C_ref[i], X[i], "group %d" % i)
