@@ -96,11 +96,7 @@ constexpr int kWaitLimit = 1 << 20;
 #ifndef NVFP4_INTERLEAVE
 #define NVFP4_INTERLEAVE 1
 #endif
-// Register ring depth (stages of B and A loads in flight) of tiles of up to
-// 4 fragments (2 or 4; larger tiles use 2, for lack of registers).
-#ifndef NVFP4_RING_SMALL
-#define NVFP4_RING_SMALL 2
-#endif
+
 #ifndef NVFP4_XCD_REMAP
 #define NVFP4_XCD_REMAP 1
 #endif
@@ -641,8 +637,10 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     // area.
     constexpr int kU = NA > kWaves ? 2 : 1;
     // Register ring depth: stage i's loads go out kRing stages ahead.
-    constexpr int kRing = MF <= 4 ? NVFP4_RING_SMALL : 2;
-    static_assert(kRing == 2 || kRing == 4, "the ring depth divides the 4-stage scale block");
+    // (Measured on MI355X: rings of 1, 2 and 4 stages time the same; the
+    // stage is bound by its issue, not by the load latency.)
+    constexpr int kRing = 2;
+    static_assert(4 % kRing == 0, "the ring depth divides the 4-stage scale block");
     uint32_t offA[2];
     h8_t* adst[2];          // k-step 0 of the unit's fragment in LDS buffer 0
     uint32_t abuf_step[2];  // bytes from buffer 0 to buffer 1 (0 for the discard area)
@@ -925,11 +923,12 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
 {
     constexpr int NA = 2 * MF;
     constexpr int kU = NA > kWaves ? 2 : 1;
-    // Stages of B in flight.  Measured on MI355X: 4 beats 8 (whose first
-    // burst of loads delays every workgroup's first stage by several us)
-    // on every workload; depths of 6 and 3 compiled to loops whose wait
-    // counts drained the ring every pass.
-    constexpr int kRing = 4;
+    // Stages of B in flight.  Measured on MI355X: 2 beats 4 and 4 beats 8
+    // on every workload (a deeper ring's first burst of loads delays every
+    // workgroup's first stage by several us, and one stage ahead already
+    // covers the load latency: a ring of 1 times the same as 2); depths of 6
+    // and 3 compiled to loops whose wait counts drained the ring every pass.
+    constexpr int kRing = 2;
     // A fragments read from LDS per group (the scheduling barrier between
     // groups keeps the compiler from loading every fragment of the stage up
     // front, which large tiles have no registers for).
