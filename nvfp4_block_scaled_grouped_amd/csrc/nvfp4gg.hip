@@ -3,8 +3,10 @@
 // C_i = A_i . B_i^T per group, A/B packed FP4 E2M1 with one E4M3 scale per 16
 // K of a row, fp32 accumulation, fp16 output (kernelindex page
 // kernelbot-nvfp4-group-gemm-444497, kernel-source header comment; page
-// kernelbot-nvfp4-group-gemm-505431, custom_kernel_fallback).  The C ABI is
-// declared in include/nvfp4gg.h.
+// kernelbot-nvfp4-group-gemm-505431, custom_kernel_fallback).  Also the same
+// GEMM with the scales in the pages' blocked layout, and its MXFP4 form (one
+// E8M0 scale per 32 K) on the block-scaled FP4 MFMA (run_segment_mx).  The
+// C ABI is declared in include/nvfp4gg.h.
 //
 // Design (gfx950 first; the pages' Blackwell kernels are prior art only):
 //   * Scale resolution: every A and B element is dequantised to fp16 as
@@ -27,7 +29,7 @@
 //     dequantised once by the workgroup into LDS as fp16, already in MFMA
 //     operand order, and the waves read it with 16-byte LDS loads.  B is
 //     private to a wave: the four lanes of a B row load its 64 stage bytes as
-//     one contiguous run straight into registers (kept three stages ahead)
+//     one contiguous run straight into registers (kept two stages ahead)
 //     and dequantise them there, so one dequantised B fragment feeds up to 12
 //     MFMAs.
 //   * K order: the sum over K is order-free.  A and B use the same order, so
@@ -39,10 +41,12 @@
 //     measured per-stage costs; a persistent grid of one workgroup per CU
 //     takes equal-cost contiguous ranges of it, so ragged groups fill the
 //     chip in one launch.  A tile whose stages span several workgroups is
-//     finished by the last of them to arrive: each writes its fp32 partial
-//     tile to a workspace slot and bumps the tile's counter; the one that
-//     sees all others done sums the partials in workgroup order
-//     (deterministic) and writes C.  No workgroup ever waits for another.
+//     finished by the first of them (whose range carries the tile's fix-up
+//     cost): the others write their fp32 partial tiles to workspace slots
+//     and count themselves in on the tile's counter; the first waits for
+//     them (bounded; on time-out it hands the fix-up over to the last to
+//     arrive), adds their partials to its own in workgroup order
+//     (deterministic) and writes C.
 //   * Loads are raw buffer loads whose range is the exact operand size, so
 //     rows past M_i or N_i read as zero without branches.
 #include <hip/hip_runtime.h>
@@ -1226,8 +1230,9 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 
 // Workspace of the split-tile fixup, one per (device, stream): three
-// partial-tile slots per workgroup and the per-tile counters (zero between calls; the last contributor
-// of a tile resets its counter).  Allocated on first use and kept.
+// partial-tile slots per workgroup and the per-tile counters (zero between
+// calls; the workgroup that finishes a tile resets its counter).  Allocated
+// on first use and kept.
 struct Workspace {
     float* partials = nullptr;
     size_t slots = 0;
