@@ -86,11 +86,6 @@ constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lg
 // A partial-slot offset past the end of every workspace (the host checks
 // that the workspace stays below it): buffer loads there return zeros.
 constexpr uint32_t kNoSlot = 0xF0000000u;
-// Split-tile counter: arrivals of the contributors after the first in the
-// low bits, the first contributor's claim of the fix-up, or its hand-over.
-constexpr int kCountMask = 0xFFFF;
-constexpr int kClaim = 1 << 16;
-constexpr int kHandOver = 1 << 17;
 // Default bound on the first contributor's wait (polls of about a
 // microsecond each).
 constexpr int kWaitLimit = 1 << 20;
@@ -453,7 +448,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         if (threadIdx.x == 0) {
             const int old =
                 __hip_atomic_fetch_add(args.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *s_flag = ((old & kCountMask) + 1 == others && (old & kHandOver)) ? 1 : 0;
+            *s_flag = other_finishes(old, others) ? 1 : 0;
         }
         __syncthreads();
         fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
@@ -462,11 +457,11 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         if (threadIdx.x == 0) {
             const int old =
                 __hip_atomic_fetch_add(args.counters + tile, kClaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            int done = (old & kCountMask) == others;
+            int done = first_finishes(old, others);
             for (int poll = 0; !done && poll < args.wait_limit; ++poll) {
                 __builtin_amdgcn_s_sleep(2);
-                done = (__hip_atomic_load(args.counters + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                        kCountMask) == others;
+                done = first_finishes(
+                    __hip_atomic_load(args.counters + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), others);
             }
             *s_flag = done;
         }
@@ -480,7 +475,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
             if (threadIdx.x == 0) {
                 const int old = __hip_atomic_fetch_add(args.counters + tile, kHandOver - kClaim, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-                *s_flag = (old & kCountMask) == others;   // the count completed meanwhile: still ours
+                *s_flag = first_finishes(old, others);   // the count completed meanwhile: still ours
             }
             __syncthreads();
             fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;

@@ -248,6 +248,26 @@ constexpr int kSlotsPerWG = 3;
 NVFP4_HD int partial_slot(int w, int w_last) { return w * kSlotsPerWG + (w < w_last ? 1 : 0); }
 NVFP4_HD int scratch_slot(int w) { return w * kSlotsPerWG + 2; }
 
+// Counter of a tile split over workgroups w_first..w_last (finish_segment):
+// arrivals of the contributors after the first in the low bits, plus the
+// first contributor's claim of the fix-up or its hand-over.  The first adds
+// kClaim, waits (bounded) until the count is complete, and on time-out swaps
+// the claim for kHandOver by adding kHandOver - kClaim; every other adds 1.
+constexpr int kCountMask = 0xFFFF;
+constexpr int kClaim = 1 << 16;
+constexpr int kHandOver = 1 << 17;
+
+// Whether the first contributor finishes the tile, given the counter value
+// it read (on claiming, while waiting, or returned by its hand-over add).
+NVFP4_HD bool first_finishes(int counter, int others) { return (counter & kCountMask) == others; }
+
+// Whether a later contributor finishes the tile, given the value its add
+// returned: its arrival completes the count after the first handed over.
+NVFP4_HD bool other_finishes(int old, int others)
+{
+    return (old & kCountMask) + 1 == others && (old & kHandOver) != 0;
+}
+
 // Global tile index of a position.
 NVFP4_HD int tile_index(const GroupSched* gs, const Pos& p)
 {
