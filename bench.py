@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--format", choices=("nvfp4", "mxfp4"), default="nvfp4",
                     help="nvfp4 (E4M3 scale per 16 K, the headline) or mxfp4 (E8M0 scale per 32 K, "
                          "mxfp4_group_gemm on the block-scaled FP4 MFMA)")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="L > 1: every group a batch of L independent products (nvfp4_group_gemm_batched)")
     ap.add_argument("--sf-layout", choices=("row-major", "blocked"), default="row-major",
                     help="scale layout: row-major (nvfp4_group_gemm) or the blocked 128 x 4 atom "
                          "layout (nvfp4_group_gemm_blocked)")
@@ -229,20 +231,41 @@ def main():
     cfg = next(c for c in workloads.CONFIGS if c["name"] == args.config)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     mx = args.format == "mxfp4"
+    if args.batch > 1 and (mx or args.sf_layout == "blocked"):
+        print("bench.py: the batched entry point takes NVFP4 row-major scales only", file=sys.stderr)
+        sys.exit(2)
     if mx and args.sf_layout == "blocked":
         print("bench.py: the MXFP4 entry point takes row-major scales only", file=sys.stderr)
         sys.exit(2)
-    abytes = workloads.algorithmic_bytes(M, N, K, 32 if mx else 16)
-    flops = workloads.algorithmic_flops(M, N, K)
+    abytes = workloads.algorithmic_bytes(M, N, K, 32 if mx else 16) * args.batch
+    flops = workloads.algorithmic_flops(M, N, K) * args.batch
     nsets = args.sets or min(64, max(1, -(-384 * 2 ** 20 // abytes)))
     blocked = args.sf_layout == "blocked"
-    sets = make_device_sets(cfg, nsets, torch, blocked, nv.blocked_scale_bytes, args.format)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    calls = [nv.GroupGemmCall(M, N, K, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
-                              [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
-                              [t.data_ptr() for t in s["C"]], sh, blocked=blocked, fmt=args.format)
-             for s in sets]
+    if args.batch > 1:
+        # Every group a batch of L slices (input variants v L .. v L + L - 1),
+        # consecutive in one allocation per operand.
+        sets = []
+        for v in range(nsets):
+            parts = [workloads.config_inputs(cfg, variant=v * args.batch + l) for l in range(args.batch)]
+            cat = lambda j, i: torch.from_numpy(np.ascontiguousarray(
+                np.concatenate([p[j][i].reshape(-1) for p in parts]))).cuda()
+            sets.append(dict(A=[cat(0, i) for i in range(len(M))], B=[cat(1, i) for i in range(len(M))],
+                             SA=[cat(2, i) for i in range(len(M))], SB=[cat(3, i) for i in range(len(M))],
+                             C=[torch.empty(args.batch * m * n, dtype=torch.float16, device="cuda")
+                                for m, n in zip(M, N)]))
+        Ls = [args.batch] * len(M)
+        calls = [(lambda s=s: nv.group_gemm_batched_ptrs(
+            M, N, K, Ls, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
+            [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]], [t.data_ptr() for t in s["C"]], sh))
+            for s in sets]
+    else:
+        sets = make_device_sets(cfg, nsets, torch, blocked, nv.blocked_scale_bytes, args.format)
+        calls = [nv.GroupGemmCall(M, N, K, [t.data_ptr() for t in s["A"]], [t.data_ptr() for t in s["B"]],
+                                  [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
+                                  [t.data_ptr() for t in s["C"]], sh, blocked=blocked, fmt=args.format)
+                 for s in sets]
 
     def step(i):
         rc = calls[i % nsets]()
@@ -302,6 +325,10 @@ def main():
                      "hbm": {"achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                              "frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": abytes}},
     }
+    if args.batch > 1:
+        out["config"]["batch_L"] = args.batch
+        out["config"]["workload"] = cfg["name"] + "_l%d" % args.batch
+        out["roofline"]["traffic"] = None
     if mx:
         # The FP4 MFMA floor (5.95 us at g8 K7168 N4096) lies far below the
         # HBM one: this form is bound by HBM.

@@ -99,6 +99,21 @@ int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,
                              const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                              void* const* C_ptrs, void* stream);
 
+/* The grouped GEMM with a batch of L_i independent products per group, the
+ * pages' (M, N, K, L) problem sizes (page 505431, custom_kernel_fallback:
+ * C[m,n,l] = sum_k A[m,k,l] B[n,k,l]; page 482006, its CuTe kernel's
+ * operand layouts, whose batch stride is the whole M x K, N x K or M x N
+ * slice): every operand of group i holds L_i consecutive slices laid out as
+ * in nvfp4_group_gemm (A_i: L_i slices of M_i x K_i/2 bytes, SFA_i: L_i of
+ * M_i x K_i/16, ..., C_i: L_i of M_i x N_i fp16), slice l of C_i being
+ * A_i[l] . B_i[l]^T.  L_i >= 0 (L_i == 0 skips the group).  Every slice must
+ * start 16-byte aligned: with L_i > 1 each slice's byte count must be a
+ * multiple of 16, else NVFP4GG_UNSUPPORTED.  Otherwise as nvfp4_group_gemm. */
+int nvfp4_group_gemm_batched(int g, const int* M, const int* N, const int* K, const int* L,
+                             const void* const* A_ptrs, const void* const* B_ptrs,
+                             const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                             void* const* C_ptrs, void* stream);
+
 /* The MXFP4 form of the grouped GEMM: the same E2M1 operands A_i, B_i and
  * fp16 output, with one E8M0 scale per 32 consecutive K of a row instead of
  * an E4M3 scale per 16:
@@ -139,8 +154,9 @@ int nvfp4_group_gemm_set_wait_limit(int polls);
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 4 (2 added nvfp4_group_gemm_blocked, 3
- * mxfp4_group_gemm, 4 nvfp4_group_gemm_set_wait_limit). */
+/* ABI version of this header: 5 (2 added nvfp4_group_gemm_blocked, 3
+ * mxfp4_group_gemm, 4 nvfp4_group_gemm_set_wait_limit, 5
+ * nvfp4_group_gemm_batched). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

@@ -39,6 +39,8 @@ def load():
     lib.nvfp4_dequant_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]
     lib.nvfp4_dequant_f16.restype = ctypes.c_int
+    lib.nvfp4_group_gemm_batched.argtypes = [ctypes.c_int, ip, ip, ip, ip, pp, pp, pp, pp, pp, ctypes.c_void_p]
+    lib.nvfp4_group_gemm_batched.restype = ctypes.c_int
     lib.nvfp4_group_gemm_set_wait_limit.argtypes = [ctypes.c_int]
     lib.nvfp4_group_gemm_set_wait_limit.restype = ctypes.c_int
     lib.nvfp4_group_gemm_last_error.argtypes = []
@@ -108,6 +110,19 @@ def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False, fmt="nv
         arr(SFB, ctypes.c_void_p), arr(C, ctypes.c_void_p), ctypes.c_void_p(stream))
 
 
+def group_gemm_batched_ptrs(M, N, K, L, A, B, SFA, SFB, C, stream=0) -> int:
+    """Raw nvfp4_group_gemm_batched call (L_i slices per group, each operand
+    holding its slices consecutively).  Returns the status code."""
+    g = len(M)
+    lib = load()
+    arr = lambda vals, ct: (ct * g)(*vals)
+    return lib.nvfp4_group_gemm_batched(
+        g, arr([int(v) for v in M], ctypes.c_int), arr([int(v) for v in N], ctypes.c_int),
+        arr([int(v) for v in K], ctypes.c_int), arr([int(v) for v in L], ctypes.c_int),
+        arr(A, ctypes.c_void_p), arr(B, ctypes.c_void_p), arr(SFA, ctypes.c_void_p),
+        arr(SFB, ctypes.c_void_p), arr(C, ctypes.c_void_p), ctypes.c_void_p(stream))
+
+
 class GroupGemmCall:
     """A grouped GEMM call whose argument arrays are marshalled once.
 
@@ -134,6 +149,26 @@ def blocked_scale_bytes(rows: int, K: int) -> int:
     """Bytes of a blocked-layout scale array of `rows` rows and K/16 scale
     columns: rows padded to a multiple of 128, columns to a multiple of 4."""
     return -(-rows // 128) * 128 * (-(-(K // 16) // 4) * 4)
+
+
+def group_gemm_batched(A, B, SFA, SFB, C, M, N, K, L, stream=None):
+    """C_i[l] = A_i[l] . B_i[l]^T for l < L_i (nvfp4_group_gemm_batched): each
+    operand a contiguous device tensor of L_i slices (A_i: L_i*M_i*K_i/2 bytes,
+    SFA_i: L_i*M_i*K_i/16, ..., C_i: L_i*M_i*N_i fp16)."""
+    g = len(A)
+    if not (len(B) == len(SFA) == len(SFB) == len(C) == len(M) == len(N) == len(K) == len(L) == g):
+        raise ValueError("operand and size lists differ in length")
+    for i in range(g):
+        need = {"A": (A[i], L[i] * M[i] * K[i] // 2), "B": (B[i], L[i] * N[i] * K[i] // 2),
+                "SFA": (SFA[i], L[i] * M[i] * K[i] // 16), "SFB": (SFB[i], L[i] * N[i] * K[i] // 16),
+                "C": (C[i], L[i] * M[i] * N[i])}
+        for name, (t, n) in need.items():
+            if t.numel() != n:
+                raise ValueError("group %d: %s has %d elements, expected %d" % (i, name, t.numel(), n))
+    _check(group_gemm_batched_ptrs(M, N, K, L, [_ptr(t, "A", _BYTES) for t in A], [_ptr(t, "B", _BYTES) for t in B],
+                                   [_ptr(t, "SFA", _BYTES) for t in SFA], [_ptr(t, "SFB", _BYTES) for t in SFB],
+                                   [_ptr(t, "C", ("float16",)) for t in C], _stream_handle(stream)))
+    return C
 
 
 def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=False, fmt="nvfp4"):

@@ -60,6 +60,7 @@
 #include <string>
 #include <type_traits>
 #include <utility>
+#include <vector>
 
 #include "nvfp4gg.h"
 #include "schedule.h"
@@ -1293,7 +1294,7 @@ int device_cus(int dev)
 
 extern "C" const char* nvfp4_group_gemm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int nvfp4_group_gemm_version(void) { return 4; }
+extern "C" int nvfp4_group_gemm_version(void) { return 5; }
 
 extern "C" int nvfp4_group_gemm_set_wait_limit(int polls)
 {
@@ -1432,6 +1433,45 @@ extern "C" int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const
                                         void* const* C_ptrs, void* stream)
 {
     return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 1, kFmtNvfp4);
+}
+
+extern "C" int nvfp4_group_gemm_batched(int g, const int* M, const int* N, const int* K, const int* L,
+                                        const void* const* A_ptrs, const void* const* B_ptrs,
+                                        const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                                        void* const* C_ptrs, void* stream)
+{
+    g_last_error.clear();
+    if (g <= 0) return fail(NVFP4GG_INVALID_ARG, "g must be >= 1");
+    if (!M || !N || !K || !L || !A_ptrs || !B_ptrs || !SFA_ptrs || !SFB_ptrs || !C_ptrs)
+        return fail(NVFP4GG_INVALID_ARG, "a size or pointer array is NULL");
+    // Every batch slice becomes a group of its own.
+    std::vector<int> eM, eN, eK;
+    std::vector<const void*> eA, eB, eSA, eSB;
+    std::vector<void*> eC;
+    for (int i = 0; i < g; ++i) {
+        const std::string gs = "group " + std::to_string(i) + ": ";
+        if (L[i] < 0 || M[i] < 0 || N[i] < 0 || K[i] < 0) return fail(NVFP4GG_INVALID_ARG, gs + "negative size");
+        if (K[i] % 16 != 0) return fail(NVFP4GG_INVALID_ARG, gs + "K must be a multiple of 16");
+        const int64_t a_bytes = (int64_t)M[i] * K[i] / 2, b_bytes = (int64_t)N[i] * K[i] / 2;
+        const int64_t sa_bytes = (int64_t)M[i] * K[i] / 16, sb_bytes = (int64_t)N[i] * K[i] / 16;
+        const int64_t c_bytes = (int64_t)M[i] * N[i] * 2;
+        if (L[i] > 1 && ((a_bytes | b_bytes | sa_bytes | sb_bytes | c_bytes) & 15) != 0)
+            return fail(NVFP4GG_UNSUPPORTED, gs + "a batch slice of an operand is not a multiple of 16 bytes, so "
+                                                  "later slices would not be 16-byte aligned");
+        for (int l = 0; l < L[i]; ++l) {
+            eM.push_back(M[i]);
+            eN.push_back(N[i]);
+            eK.push_back(K[i]);
+            eA.push_back(static_cast<const uint8_t*>(A_ptrs[i]) + l * a_bytes);
+            eB.push_back(static_cast<const uint8_t*>(B_ptrs[i]) + l * b_bytes);
+            eSA.push_back(static_cast<const uint8_t*>(SFA_ptrs[i]) + l * sa_bytes);
+            eSB.push_back(static_cast<const uint8_t*>(SFB_ptrs[i]) + l * sb_bytes);
+            eC.push_back(static_cast<uint8_t*>(C_ptrs[i]) + l * c_bytes);
+        }
+    }
+    if (eM.empty()) return NVFP4GG_OK;
+    return group_gemm_impl((int)eM.size(), eM.data(), eN.data(), eK.data(), eA.data(), eB.data(), eSA.data(),
+                           eSB.data(), eC.data(), stream, 0, kFmtNvfp4);
 }
 
 extern "C" int mxfp4_group_gemm(int g, const int* M, const int* N, const int* K, const void* const* A_ptrs,

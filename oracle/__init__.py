@@ -248,6 +248,31 @@ def group_gemm(M, N, K, A, B, SFA, SFB, *, exact: bool = False,
     return (C, X) if exact else C
 
 
+def group_gemm_batched(M, N, K, L, A, B, SFA, SFB, *, exact: bool = False, nthreads: int = 0):
+    """The batched form, (M, N, K, L) per group (page 505431,
+    custom_kernel_fallback: C[m,n,l] = sum_k A[m,k,l] B[n,k,l]; page 482006:
+    the batch stride is a whole slice): slice l of every operand is the l-th
+    consecutive block of its array, and each slice is the ordinary product.
+    Returns per group the list of L_i fp16 outputs (and exact sums)."""
+    C, X = [], []
+    for i in range(len(M)):
+        m, n, k, l_count = M[i], N[i], K[i], L[i]
+        a = np.ascontiguousarray(A[i], dtype=np.uint8).reshape(-1)
+        b = np.ascontiguousarray(B[i], dtype=np.uint8).reshape(-1)
+        sa = np.ascontiguousarray(SFA[i], dtype=np.uint8).reshape(-1)
+        sb = np.ascontiguousarray(SFB[i], dtype=np.uint8).reshape(-1)
+        sl = lambda arr, size, j: arr[j * size:(j + 1) * size]
+        Ms, Ns, Ks = [m] * l_count, [n] * l_count, [k] * l_count
+        out = group_gemm(Ms, Ns, Ks, [sl(a, m * k // 2, j) for j in range(l_count)],
+                         [sl(b, n * k // 2, j) for j in range(l_count)],
+                         [sl(sa, m * k // 16, j) for j in range(l_count)],
+                         [sl(sb, n * k // 16, j) for j in range(l_count)], exact=True, nthreads=nthreads) \
+            if l_count else ([], [])
+        C.append(out[0])
+        X.append(out[1])
+    return (C, X) if exact else C
+
+
 def gemm_element(M, N, K, A, B, SFA, SFB, m, n):
     """One output element of a single group: (fp16 bits, exact value)."""
     c16 = ctypes.c_uint16()

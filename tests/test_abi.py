@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert nv.version() == 4
+    assert nv.version() == 5
 
 
 A16 = 0x10000          # fake, aligned addresses: never dereferenced, every case
@@ -140,3 +140,15 @@ def test_mxfp4_entry_validates(lib):
 def test_wait_limit_validation(lib):
     assert lib.nvfp4_group_gemm_set_wait_limit(-1) == nv.INVALID_ARG
     assert lib.nvfp4_group_gemm_set_wait_limit(1 << 20) == nv.OK
+
+
+def test_batched_entry_validates(lib):
+    ip = lambda v: (ctypes.c_int * len(v))(*v)
+    pp = lambda v: (ctypes.c_void_p * len(v))(*v)
+    f = lib.nvfp4_group_gemm_batched
+    assert f(0, None, None, None, None, None, None, None, None, None, None) == nv.INVALID_ARG
+    args = lambda M, N, K, L: (1, ip([M]), ip([N]), ip([K]), ip([L]), pp([A16]), pp([A16]), pp([A16]), pp([A16]),
+                               pp([A16]), None)
+    assert f(*args(8, 8, 256, -1)) == nv.INVALID_ARG
+    assert f(*args(3, 8, 128, 2)) == nv.UNSUPPORTED and "16 bytes" in nv.last_error()   # SFA slice of 24 bytes
+    assert f(*args(8, 8, 256, 0)) == nv.OK                                                # no slices: nothing to do

@@ -458,3 +458,32 @@ def test_mx_pins_detect_plausible_mistakes(oracle_lib):
     C = oracle_lib.mx_group_gemm([M], [N], [K], A, B, SA, SB, exact=True)[1][0]
     assert not np.array_equal(C * 2.0, base)
     np.testing.assert_array_equal(C, base)
+
+
+# ------------------------------------------------------------------ batched
+
+def test_batched_is_independent_slices(oracle_lib):
+    """(M, N, K, L) problems: slice l of every operand is its l-th consecutive
+    block, and each output slice is the single product of those slices
+    (checked against separate single-problem calls); changing one slice of
+    A changes that output slice only."""
+    M, N, K, L = [5, 9], [7, 3], [128, 256], [3, 2]
+    A, B, SA, SB = [], [], [], []
+    for i in range(2):
+        parts = [workloads.make_group(40 + l, i, M[i], N[i], K[i]) for l in range(L[i])]
+        A.append(np.concatenate([p[0].reshape(-1) for p in parts]))
+        B.append(np.concatenate([p[1].reshape(-1) for p in parts]))
+        SA.append(np.concatenate([p[2].reshape(-1) for p in parts]))
+        SB.append(np.concatenate([p[3].reshape(-1) for p in parts]))
+    C = oracle_lib.group_gemm_batched(M, N, K, L, A, B, SA, SB)
+    for i in range(2):
+        for l in range(L[i]):
+            p = workloads.make_group(40 + l, i, M[i], N[i], K[i])
+            want = oracle_lib.group_gemm([M[i]], [N[i]], [K[i]], [p[0]], [p[1]], [p[2]], [p[3]])[0]
+            np.testing.assert_array_equal(C[i][l].view(np.uint16), want.view(np.uint16))
+    A2 = [a.copy() for a in A]
+    A2[0][M[0] * K[0] // 2: 2 * M[0] * K[0] // 2] ^= 0x11          # slice 1 of group 0
+    C2 = oracle_lib.group_gemm_batched(M, N, K, L, A2, B, SA, SB)
+    assert not np.array_equal(C2[0][1].view(np.uint16), C[0][1].view(np.uint16))
+    for i, l in [(0, 0), (0, 2), (1, 0), (1, 1)]:
+        np.testing.assert_array_equal(C2[i][l].view(np.uint16), C[i][l].view(np.uint16))
