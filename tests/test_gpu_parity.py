@@ -105,7 +105,7 @@ def test_dequant_exhaustive(nv, oracle_lib, K):
 # ------------------------------------------------------------ small / medium
 
 def test_config1_full(nv, oracle_lib):
-    cfg = workloads.CONFIGS[0]
+    cfg = workloads.SMALL
     _full_parity(nv, oracle_lib, cfg["M"], cfg["N"], cfg["K"], cfg["seed"])
 
 

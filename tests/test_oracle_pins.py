@@ -167,7 +167,7 @@ def test_bruteforce_random_scales(oracle_lib, dist, shape):
 
 
 def test_int64_and_f64_paths_agree_on_config_inputs(oracle_lib):
-    cfg = workloads.CONFIGS[0]
+    cfg = workloads.SMALL
     A, B, SA, SB = workloads.config_inputs(cfg)
     C1, X1 = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB, exact=True)
     C2, X2 = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB,
@@ -180,7 +180,7 @@ def test_int64_and_f64_paths_agree_on_config_inputs(oracle_lib):
 def test_config1_matches_bruteforce(oracle_lib):
     """The whole small workload against float64 matmul: products are multiples
     of 2^-14 below 2^13, K = 512, so sums stay below 2^22 / 2^-14 = 2^36."""
-    cfg = workloads.CONFIGS[0]
+    cfg = workloads.SMALL
     A, B, SA, SB = workloads.config_inputs(cfg)
     C = oracle_lib.group_gemm(cfg["M"], cfg["N"], cfg["K"], A, B, SA, SB)
     for i in range(cfg["g"]):

@@ -91,7 +91,18 @@ CONFIGS = [
     dict(name="g8_k7168_n4096", g=8, M=[80, 176, 128, 72, 64, 248, 96, 160],
          N=[4096] * 8, K=[7168] * 8, seed=1111),
 ]
-HEADLINE = CONFIGS[4]
+
+
+def config(name: str) -> dict:
+    """The workload called ``name`` (one of CONFIGS' names)."""
+    for cfg in CONFIGS:
+        if cfg["name"] == name:
+            return cfg
+    raise KeyError("unknown workload %r" % name)
+
+
+SMALL = config("g2_k512_n256")
+HEADLINE = config("g8_k7168_n4096")
 
 _T_A, _T_B, _T_SFA, _T_SFB = 1, 2, 3, 4
 
