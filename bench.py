@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--sf-layout", choices=("row-major", "blocked"), default="row-major",
                     help="scale layout: row-major (nvfp4_group_gemm) or the blocked 128 x 4 atom "
                          "layout (nvfp4_group_gemm_blocked)")
+    ap.add_argument("--launch-per-group", action="store_true",
+                    help="one launch per group instead of one grouped launch (for comparison)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -234,6 +236,9 @@ def main():
     if args.batch > 1 and (mx or args.sf_layout == "blocked"):
         print("bench.py: the batched entry point takes NVFP4 row-major scales only", file=sys.stderr)
         sys.exit(2)
+    if args.launch_per_group and args.batch > 1:
+        print("bench.py: --launch-per-group takes batch L = 1", file=sys.stderr)
+        sys.exit(2)
     if mx and args.sf_layout == "blocked":
         print("bench.py: the MXFP4 entry point takes row-major scales only", file=sys.stderr)
         sys.exit(2)
@@ -266,6 +271,23 @@ def main():
                                   [t.data_ptr() for t in s["SA"]], [t.data_ptr() for t in s["SB"]],
                                   [t.data_ptr() for t in s["C"]], sh, blocked=blocked, fmt=args.format)
                  for s in sets]
+        if args.launch_per_group:
+            # The same products as g launches of one group each, back to
+            # back on one stream: what a grouped launch saves.
+            def per_group(s):
+                one = [nv.GroupGemmCall(M[i:i + 1], N[i:i + 1], K[i:i + 1], [s["A"][i].data_ptr()],
+                                        [s["B"][i].data_ptr()], [s["SA"][i].data_ptr()],
+                                        [s["SB"][i].data_ptr()], [s["C"][i].data_ptr()], sh,
+                                        blocked=blocked, fmt=args.format) for i in range(len(M))]
+
+                def run():
+                    for c in one:
+                        rc = c()
+                        if rc != nv.OK:
+                            return rc
+                    return nv.OK
+                return run
+            calls = [per_group(s) for s in sets]
 
     def step(i):
         rc = calls[i % nsets]()
@@ -340,6 +362,10 @@ def main():
                                     "unit": "TFLOP/s", "frac": round(tflops / FP4_MFMA_PEAK_TFLOPS, 4)}}
         out["dtype"] = "fp4"
         out["metric"] = METRIC.replace("NVFP4", "MXFP4")
+    if args.launch_per_group:
+        out["config"]["launches"] = "one per group"
+        out["config"]["workload"] = cfg["name"] + "_per_group_launches"
+        out["roofline"]["traffic"] = None
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, args.format)
     print(json.dumps(out), flush=True)
