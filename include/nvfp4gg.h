@@ -28,15 +28,15 @@
  *
  * Library state: tiles whose K range is split over several workgroups are
  * summed through a device workspace (fp32 partial tiles and one counter per
- * tile) that the library allocates with hipMalloc on the first call for a
- * (device, stream) pair and keeps, growing it when a later call needs more
- * (that call synchronises the stream first), until the process ends.  At
- * most 3 x (compute units) x 192 KiB of partials plus 4 bytes per tile
- * (16 KiB at least).  The counters return to zero at the end of every call,
- * so calls on one stream may follow each other with no reset; calls on
- * different streams use different workspaces.  A call that must allocate is
- * not capturable into a HIP graph; once the workspace of a stream exists,
- * calls of the same or smaller size on it allocate nothing.
+ * workgroup) that the library allocates with hipMalloc on the first call for
+ * a (device, stream) pair, sized for the device's compute units (no launch
+ * has more workgroups), and keeps until the process ends: 3 partial tiles of
+ * 96 KiB and one int per compute unit (72 MiB and 1 KiB on a 256-CU MI355X).
+ * Only that first call allocates (and is not capturable into a HIP graph);
+ * every later call on the pair allocates, frees and synchronises nothing.
+ * The counters return to zero at the end of every call, so calls on one
+ * stream may follow each other with no reset; calls on different streams
+ * use different workspaces.
  *
  * Streams: work is enqueued on `stream` (a hipStream_t; NULL is the default
  * stream) and the call returns without synchronising.
@@ -49,7 +49,7 @@
  *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle: a
  *                            non-empty group with K_i % 128 != 0, an operand
  *                            of 2 GiB or more, or M_i * N_i >= 2^31
- *   NVFP4GG_HIP_ERROR    -3  a HIP call (launch, workspace allocation) failed
+ *   NVFP4GG_HIP_ERROR    -3  a HIP call (launch, first-call workspace allocation) failed
  * nvfp4_group_gemm_last_error() describes the last failure on this thread.
  */
 #ifndef NVFP4GG_H
@@ -151,12 +151,21 @@ int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
  * Returns NVFP4GG_INVALID_ARG for a negative count. */
 int nvfp4_group_gemm_set_wait_limit(int polls);
 
+/* The m-block size, in fragments of 16 rows (1..6), used for every launch
+ * (process-wide); 0 (the default) chooses it per launch from the problem
+ * sizes.  Results do not depend on it beyond fp32 rounding order (each
+ * output is one fp32 sum of exact products in every case); it exists for
+ * tuning and so that tests can run every tile shape.  Returns
+ * NVFP4GG_INVALID_ARG for a value outside 0..6. */
+int nvfp4_group_gemm_set_max_frags(int frags);
+
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 5 (2 added nvfp4_group_gemm_blocked, 3
+/* ABI version of this header: 6 (2 added nvfp4_group_gemm_blocked, 3
  * mxfp4_group_gemm, 4 nvfp4_group_gemm_set_wait_limit, 5
- * nvfp4_group_gemm_batched). */
+ * nvfp4_group_gemm_batched, 6 nvfp4_group_gemm_set_max_frags and the
+ * workspace that no longer grows). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

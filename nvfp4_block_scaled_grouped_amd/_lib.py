@@ -43,6 +43,8 @@ def load():
     lib.nvfp4_group_gemm_batched.restype = ctypes.c_int
     lib.nvfp4_group_gemm_set_wait_limit.argtypes = [ctypes.c_int]
     lib.nvfp4_group_gemm_set_wait_limit.restype = ctypes.c_int
+    lib.nvfp4_group_gemm_set_max_frags.argtypes = [ctypes.c_int]
+    lib.nvfp4_group_gemm_set_max_frags.restype = ctypes.c_int
     lib.nvfp4_group_gemm_last_error.argtypes = []
     lib.nvfp4_group_gemm_last_error.restype = ctypes.c_char_p
     lib.nvfp4_group_gemm_version.argtypes = []
@@ -223,6 +225,12 @@ def set_wait_limit(polls: int):
     """Bound on a split tile's finisher waiting for the other contributors
     (see include/nvfp4gg.h); 0 hands every fix-up to the last arriver."""
     _check(load().nvfp4_group_gemm_set_wait_limit(int(polls)))
+
+
+def set_max_frags(frags: int):
+    """m-block size (fragments of 16 rows, 1..6) forced for every launch;
+    0 chooses it per launch (see include/nvfp4gg.h)."""
+    _check(load().nvfp4_group_gemm_set_max_frags(int(frags)))
 
 
 def version() -> int:

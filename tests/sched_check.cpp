@@ -56,6 +56,7 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
     std::map<std::pair<int, int>, int> covered;
     std::map<int, std::set<int>> contrib;         // tile -> workgroups
     std::map<std::pair<int, int>, int> slot_use;  // (wg, slot) -> tile
+    std::map<int, int> counter_use;               // counter index -> split tile
     for (int w = 0; w < G; ++w) {
         const int64_t b1 = boundary(W, G, w + 1);
         Pos pos = locate(gs, ng, boundary(W, G, w));
@@ -82,6 +83,13 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
             const int wf = owner(W, G, c_first), wl = owner(W, G, c_last);
             CHECK(wf <= w && w <= wl, "contributor range");
             if (wf != wl) {
+                // one counter per split tile, indexed by its first contributor
+                const int ci = counter_index(wf);
+                CHECK(ci >= 0 && ci < G, "counter index %d outside [0, %d)", ci, G);
+                auto cu = counter_use.find(ci);
+                CHECK(cu == counter_use.end() || cu->second == t, "counter %d shared by tiles %d and %d", ci,
+                      cu == counter_use.end() ? -1 : cu->second, t);
+                counter_use[ci] = t;
                 const int slot = partial_slot(w, wl);
                 auto sk = std::make_pair(w, slot);
                 CHECK(!slot_use.count(sk), "slot reused w=%d slot=%d", w, slot);
