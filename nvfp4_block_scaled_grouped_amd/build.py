@@ -12,11 +12,15 @@ LIB = os.path.join(PKG, "libnvfp4gg.so")
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are switched off for all device code; the compiler
-# otherwise forms them from plain float code.
+# otherwise forms them from plain float code.  MFMA accumulators are kept in
+# VGPRs: with the unified register file of gfx950 that lets the register
+# allocator share a wave's 256 registers between accumulators and operands
+# as the kernel needs (AGPR accumulators cap the VGPRs at 128).
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared",
     "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-Wall",
 ]
 

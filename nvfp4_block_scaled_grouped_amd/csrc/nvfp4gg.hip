@@ -83,8 +83,9 @@ constexpr int kWaves = 8;                    // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
 constexpr int kColGroups = 4;                // waves per K half
 constexpr int kColFrags = kTileN / kColGroups / 16;   // 16-column B fragments per wave
-constexpr int kKSteps = kStageK / 32;        // MFMA k-steps per stage (32 K each)
-constexpr int kMaxChainStages = 128;         // stages of one chain (64 per K half: 8192 K)
+constexpr int kKSteps = kStageK / 2 / 32;    // MFMA k-steps of one K half of a stage (32 K each)
+constexpr int kStageBytes = kStageK / 2;     // bytes of a row per stage
+constexpr int kMaxChainStages = 64;          // stages of one chain (8192 K per K half)
 constexpr uint32_t kPieceBytes = kWave * 16; // one wave's 16 x 16 fp32 block
 // One fp32 partial tile: every (column group, fragment, column fragment)
 // piece at a fixed place, whatever the tile's fragment count.
@@ -96,9 +97,39 @@ constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lg
 constexpr int kWaitLimit = 1 << 20;
 
 static_assert(kColFrags == 4, "a wave owns 64 columns: four 16-column B fragments");
-static_assert(kKSteps == 4, "a stage is one 16-byte piece of 4 k-steps per lane");
+static_assert(kKSteps == 4, "a K half of a stage is one 16-byte piece of 4 k-steps per lane");
 static_assert(kFragRows == 16, "fragments are the MFMA's 16 rows");
 static_assert(kMaxFrags == 6, "the kernels instantiate tiles of 1 to 6 fragments");
+
+// LDS of one workgroup (byte offsets).  NVFP4: two buffers of the
+// dequantised A of a stage, two blocks of staged scales (two stages of the
+// tile's B rows and A rows each), and the raw A codes of the next stage
+// (one slot per piece, each used by one wave only).  MXFP4: the same with raw A codes and
+// E8M0 scales.  At the end of a segment the first kRedBytes carry the
+// exchange of the two K halves' accumulators.
+constexpr uint32_t kAFragBytes = 2 * kKSteps * kWave * 16;        // [K half][k-step][lane] x 8 fp16
+constexpr uint32_t kABufBytes = kMaxFrags * kAFragBytes;          // 48 KB
+constexpr uint32_t kSRow = 2 * kStageK / 16;                      // E4M3 bytes of a row per block
+constexpr uint32_t kSBBytes = kTileN * kSRow;                     // also two 128-row bands of 8 atoms
+constexpr uint32_t kSABytes = kSBBytes;                           // the A rows' bands likewise
+constexpr uint32_t kSBlockBytes = kSBBytes + kSABytes;
+constexpr uint32_t kNvScaleOff = 2 * kABufBytes;
+constexpr uint32_t kNvRawOff = kNvScaleOff + 2 * kSBlockBytes;    // raw A of the next stage, one slot per piece
+constexpr uint32_t kNvLds = kNvRawOff + 2 * kMaxFrags * kPieceBytes;
+
+constexpr uint32_t kMxAFragBytes = 2 * kWave * 16;                // [K half][lane] x 32 codes
+constexpr uint32_t kMxABufBytes = kMaxFrags * kMxAFragBytes;
+constexpr uint32_t kMxSRow = 2 * kStageK / 32;                    // E8M0 bytes of a row per block
+constexpr uint32_t kMxSBBytes = kTileN * kMxSRow;
+constexpr uint32_t kMxSABytes = kMaxFrags * kFragRows * kMxSRow;
+constexpr uint32_t kMxSBlockBytes = kMxSBBytes + kMxSABytes;
+constexpr uint32_t kMxScaleOff = 2 * kMxABufBytes;
+constexpr uint32_t kMxLds = kMxScaleOff + 2 * kMxSBlockBytes;
+
+constexpr uint32_t kRedBytes = kColGroups * kMaxFrags * kColFrags * kPieceBytes;
+constexpr uint32_t kLdsBytes = kNvLds > kRedBytes ? (kNvLds > kMxLds ? kNvLds : kMxLds)
+                                                  : (kRedBytes > kMxLds ? kRedBytes : kMxLds);
+static_assert(kLdsBytes <= 160 * 1024, "the LDS of one workgroup fits a CU");
 
 struct GroupArgs {
     const uint8_t* A;
@@ -162,41 +193,10 @@ __device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
     return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-__device__ __forceinline__ uint8_t load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-}
+// A per-lane offset that is out of range of every buffer (operands are
+// smaller than 2 GiB): the load reads nothing and returns zeros.
+constexpr uint32_t kNoLoad = 0x80000000u;
 
-// LDS image of the dequantised A rows of one stage, in MFMA operand order:
-// [16-row fragment][k-step][lane] x 8 fp16 (32 KB).
-struct AStage {
-    h8_t v[kMaxFrags][kKSteps][kWave];
-};
-
-// MXFP4: the raw A codes of a stage in MFMA operand order (16 bytes per lane
-// per fragment) and each lane's E8M0 scale byte.
-struct MxStage {
-    i4_t v[kMaxFrags][kWave];
-    uint32_t s[kMaxFrags][kWave];
-};
-
-// The workgroup's LDS: the double-buffered A stage (NVFP4: both K halves
-// read the same stage; MXFP4: each K half its own); at the end of a segment
-// the same memory carries the exchange of the two K halves' accumulators.
-struct SharedMem {
-    union {
-        AStage a[2];        // [stage parity]
-        MxStage mx[2][2];   // [K half][stage parity]
-        f4_t red[kColGroups][kMaxFrags][kColFrags][kWave];
-    };
-    // Target of the A pieces of a wave's unit past the tile's fragments
-    // (their writes are discarded), so the k-step needs no branch.
-    h8_t discard[kKSteps][kWave];
-};
-static_assert(sizeof(SharedMem) <= 160 * 1024, "the LDS of one workgroup fits a CU");
-static_assert(sizeof(MxStage) <= sizeof(AStage), "MXFP4 stages fit the NVFP4 ones");
-static_assert(sizeof(i4_t) * kWave + sizeof(uint32_t) * kWave <= sizeof(h8_t) * kKSteps * kWave,
-              "the discard area holds an MXFP4 piece");
 
 // fp16 round-to-nearest-even (overflow to inf) of 4 floats, packed.
 __device__ __forceinline__ uint2 pack4(f4_t v)
@@ -248,17 +248,16 @@ __device__ __forceinline__ void fence_after(const T& v)
     asm volatile("" ::"v"(v) : "memory");
 }
 
-// Keeps the accumulators in AGPRs across a stage boundary: an empty asm with
-// AGPR operands, so the register allocator gives every accumulator one AGPR
-// home for the whole loop instead of moving some through VGPRs between the
-// unrolled stages.
+// Keeps every accumulator in a register across a stage boundary (an empty
+// asm that reads and writes it), so the unrolled stages do not move
+// accumulators around between them.
 template <int F>
-__device__ __forceinline__ void pin_agprs(f4_t (*acc)[4])
+__device__ __forceinline__ void pin_acc(f4_t (*acc)[4])
 {
 #pragma unroll
     for (int a = 0; a < F; ++a)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) asm volatile("" : "+a"(acc[a][f]));
+        for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(acc[a][f]));
 }
 
 // The worker index of this workgroup.  Workgroups are dispatched round-robin
@@ -301,18 +300,18 @@ struct Half {
 };
 
 template <int F, int KH>
-__device__ __forceinline__ void exchange_halves(SharedMem& sm, f4_t (*acc)[kColFrags], int cg, int lane)
+__device__ __forceinline__ void exchange_halves(uint8_t* lds, f4_t (*acc)[kColFrags], int cg, int lane)
 {
     using H = Half<F, KH>;
 #pragma unroll
     for (int a = H::other_lo; a < H::other_hi; ++a)
 #pragma unroll
-        for (int f = 0; f < kColFrags; ++f) sm.red[cg][a][f][lane] = acc[a][f];
+        for (int f = 0; f < kColFrags; ++f) *reinterpret_cast<f4_t*>(lds + piece_off(cg, a, f, lane)) = acc[a][f];
     lds_barrier();
 #pragma unroll
     for (int a = H::lo; a < H::hi; ++a)
 #pragma unroll
-        for (int f = 0; f < kColFrags; ++f) acc[a][f] += sm.red[cg][a][f][lane];
+        for (int f = 0; f < kColFrags; ++f) acc[a][f] += *reinterpret_cast<const f4_t*>(lds + piece_off(cg, a, f, lane));
     lds_barrier();   // the exchange area is the next segment's A stages
 }
 
@@ -388,10 +387,10 @@ __device__ __forceinline__ void store_c(const GroupArgs& ga, int m0, int n0, con
 // by the tile's first contributor).
 template <int F, int KH>
 __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos& pos, bool first_chain,
-                                               bool last_chain, SharedMem& sm, int* s_flag,
+                                               bool last_chain, uint8_t* lds, int* s_flag,
                                                f4_t (*acc)[kColFrags], int m0, int n0, int cg, int lane)
 {
-    exchange_halves<F, KH>(sm, acc, cg, lane);
+    exchange_halves<F, KH>(lds, acc, cg, lane);
 
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
@@ -511,9 +510,10 @@ __device__ __forceinline__ void pair_pass(Fn& f, int i)
 //
 // One chain [s_begin, s_end) of the stages of a tile with F fragments: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
-// stages; first_chain / last_chain place this chain in its segment.  All 8
-// waves work on the same stage; the waves of K half kh run its k-steps
-// 2 kh and 2 kh + 1.
+// stages; first_chain / last_chain place this chain in its segment.  A stage
+// is 256 K: 128 bytes of every A and B row and 16 scale bytes.  All 8 waves
+// work on the same stage; K half kh of a stage is its row bytes
+// [64 kh, 64 kh + 64), run by the 4 waves of half kh as 4 k-steps.
 //
 // MFMA: v_mfma_f32_16x16x32_f16 with B as the first operand (16 columns of
 // B_i) and A as the second (16 rows of A_i).  Lane (c16, kq) = (lane % 16,
@@ -521,31 +521,45 @@ __device__ __forceinline__ void pair_pass(Fn& f, int i)
 // 4 kq .. 4 kq + 3 of the first operand's side, i.e. output row c16 and
 // output columns 4 kq .. 4 kq + 3 of the 16 x 16 block.
 //
-// K order within a stage (128 K, 64 bytes of a row; the sum is order-free
-// and A and B use the same order): at k-step v = 2 h + b lane (c16, kq)
-// holds the 8 codes at K 64 h + 16 kq + 8 b, i.e. dword b of the 8 bytes
-// [32 h + 8 kq, +8) of the row's stage bytes, whose scale block is
-// 4 h + kq.  So a wave of K half h reads, per B row and stage, the 32
-// contiguous bytes [32 h, 32 h + 32) (the two halves together the row's 64
-// stage bytes) and one scale byte per lane.
+// K order within a K half (the sum is order-free; A and B use the same
+// order): at k-step v lane (c16, kq) holds dword v of the 16 bytes
+// [64 kh + 16 kq, +16) of its row's stage bytes, whose scale is byte
+// 8 kh + 2 kq + v / 2 of the row's 16 stage scale bytes.  So every lane
+// loads 16 contiguous bytes of B per fragment and stage, the four lanes of
+// a row one 64-byte run.
 //
-// A: fragment a of a stage is dequantised by wave a (for a < F), which
-// loads 16 bytes of its row per lane, lane (c16, j) the bytes [16 j, +16):
-// its dword d holds the codes of k-step 2 (j / 2) + d % 2 for consumer lane
-// c16 + 16 (2 (j % 2) + d / 2), with scale block 2 j + d / 2.
+// A: the 2 F pieces of a stage (fragment a, K half h: 16 rows x 64 bytes)
+// are dequantised by the waves, piece p by wave p % 8; lane (c16, kq) of it
+// loads the same 16 bytes that consumer lane (c16, kq) of K half h needs
+// and writes dword v, dequantised, as that lane's operand of k-step v.
+//
+// Scales: the scale bytes of a block of two stages of the tile's B rows and
+// A rows are loaded by all threads (16 contiguous bytes per thread), one
+// stage later written to one of two LDS blocks, and read from there: B's by
+// their consumers, A's by the producers.  A tile that ends with a 128-K
+// stage gets zero scales for the missing half of that stage, so its codes
+// (the next row's, or zeros past the buffer) contribute exact zeros.
 //
 // Pipeline, per stage t of the chain (register ring slot p = t % 2):
-//   * B of stage t is in bq[p], bs[p] (loaded two stages earlier); it is
-//     re-loaded with stage t + 2 once dequantised.
-//   * A of stage t is in LDS buffer p.  The raw A of stage t + 1 (aq[p],
-//     as[p], loaded two stages earlier) is dequantised into the other
-//     buffer during the MFMAs, then re-loaded with stage t + 3.
+//   * B of stage t is in bq[p] (loaded two stages earlier).  The B operands
+//     of a k-step are dequantised during the MFMAs of the previous one
+//     (those of k-step 0 during k-step 3 of the stage before); the slot is
+//     re-loaded with stage t + 2 once its last dword is dequantised.
+//   * A of stage t is in LDS buffer p.  The raw A of stage t + 1 (in the
+//     wave's raw LDS slot) is dequantised into the other buffer, one dword
+//     per k-step; the raw A of stage t + 2, loaded at the start of the
+//     stage, replaces it in the slot at the end.
+//   * Scale block b (stages 2 b, 2 b + 1) is loaded during stage 2 b - 3
+//     and written during stage 2 b - 2 into LDS block b % 2; it is read
+//     from stage 2 b - 1 on (the B look-ahead and the A production read the
+//     next stage's scales), and block b - 2 was last read in stage 2 b - 4.
 //   * One LDS-only barrier ends the stage.
 template <int F, bool kBlocked, int KH>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
-                                            bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
+                                            bool first_chain, bool last_chain, uint8_t* lds, int* s_flag)
 {
     constexpr int kh = KH;
+    constexpr int kP = F > 4 ? 2 : 1;   // A pieces per wave: pieces w and w + 8 of 2 F
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
@@ -558,162 +572,275 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 16;
+    const int last_stage = gs.stages - 1;
+    const bool half_last = (K % kStageK) != 0;   // the tile's last stage holds 128 K
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
-    // Scale column c (stage 0) of row r.  Row-major: byte r K/16 + c; a
-    // stage advances 8 bytes.  Blocked (the 128 x 4 atom layout): byte
-    // 512 ((r / 128) (K / 64) + c / 4) + 16 (r % 32) + 4 ((r / 32) % 4)
-    // + c % 4; a stage advances 2 atoms.
-    auto sf_off = [&](uint32_t r, uint32_t c) {
-        return kBlocked ? (r >> 7) * (uint32_t)K * 8u + (r & 31u) * 16u + ((r >> 5) & 3u) * 4u + 512u * (c >> 2) +
-                              (c & 3u)
-                        : r * row_scales + c;
-    };
-    constexpr uint32_t kScaleStride = kBlocked ? 1024u : (uint32_t)kStageK / 16;
+    // Blocked scale arrays hold whole 128-row bands.
+    const uint32_t sa_rows = kBlocked ? (uint32_t)(M + 127) / 128u * 128u : (uint32_t)M;
+    const uint32_t sb_rows = kBlocked ? (uint32_t)(N + 127) / 128u * 128u : (uint32_t)N;
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, sa_rows * row_scales);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, sb_rows * row_scales);
 
     // B operand of lane (c16, kq) in fragment f: row n0 + 64 cg + 16 f + c16
-    // (rows past N read 0), bytes [32 kh + 8 kq, +8), scale column 4 kh + kq.
-    // Scale bytes are read with plain global loads (their zero extension is
-    // part of the load instruction, so no separate instruction touches the
-    // loaded register before it is needed); rows past N are clamped to the
-    // last row, whose products only reach columns that are never stored.
-    uint32_t offB[kColFrags], offSB[kColFrags];
+    // (rows past N read 0), bytes [64 kh + 16 kq, +16) of each stage.
+    uint32_t offB[kColFrags];
 #pragma unroll
-    for (int f = 0; f < kColFrags; ++f) {
-        const uint32_t brow = (uint32_t)(n0 + 64 * cg + 16 * f + c16);
-        offB[f] = brow * row_bytes + 32u * kh + 8u * kq;
-        offSB[f] = sf_off(brow < (uint32_t)N ? brow : (uint32_t)N - 1, 4u * kh + kq);
-    }
-    // This wave's A fragment (wave < F): row m0 + 16 wave + c16, bytes
-    // [16 j, +16) with j = kq, scale columns 2 j, 2 j + 1.  A wave past the
-    // tile's fragments loads fragment 0's rows (cache hits) and writes the
-    // discard area.  Rows past M read 0 (codes) or are clamped (scales).
-    const bool areal = wave < F;
-    const uint32_t arow = (uint32_t)(m0 + 16 * (areal ? wave : 0) + c16);
-    const uint32_t offA = arow * row_bytes + 16u * kq;
-    const uint32_t offSA = sf_off(arow < (uint32_t)M ? arow : (uint32_t)M - 1, 2u * kq);
-    // LDS targets of the four dwords of this lane's 16 bytes (buffer 0):
-    // dword d goes to k-step 2 (kq / 2) + d % 2 of consumer lane
-    // c16 + 16 (2 (kq % 2) + d / 2).
-    h8_t* adst[4];
+    for (int f = 0; f < kColFrags; ++f)
+        offB[f] = (uint32_t)(n0 + 64 * cg + 16 * f + c16) * row_bytes + 64u * kh + 16u * kq;
+    // Staged scales (both layouts: thread t copies 16 bytes to byte 16 t of
+    // the block's B part, and of its A part).  Row-major: the B part is
+    // [row][32 bytes], the row's 16 scale bytes of each of the two stages;
+    // the A part likewise for the tile's rows.  Blocked: the B part is the
+    // two 128-row bands of the tile's B rows, 8 atoms of 512 bytes each (4
+    // scale columns of 128 rows; the 4 atoms of a stage in column order,
+    // stage 0 first); the A part the same for the two bands from the one
+    // holding row m0.  Byte offset of (row r, scale column c of stage part
+    // q) in a part:
+    //   row-major: 32 r + 16 q + c
+    //   blocked:   512 (8 (r / 128) + 4 q + c / 4) + 16 (r % 32) + 4 ((r / 32) % 4) + c % 4
+    auto sf_lds = [&](uint32_t r, uint32_t c) -> uint32_t {
+        return kBlocked ? 512u * (8u * (r >> 7) + (c >> 2)) + 16u * (r & 31u) + 4u * ((r >> 5) & 3u) + (c & 3u)
+                        : kSRow * r + c;
+    };
+    constexpr uint32_t kPartStride = kBlocked ? 2048u : 16u;   // stage part 1 of a block
+    // This lane's B scales: tile row 64 cg + 16 f + c16, column 8 kh + 2 kq
+    // (two bytes: k-steps 0-1 and 2-3).  Fragment f adds sfb_frag(f).
+    const uint32_t sbsrc = kNvScaleOff + sf_lds((uint32_t)(64 * cg + c16), 8u * kh + 2u * kq);
+    auto sfb_frag = [&](int f) -> uint32_t {
+        return kBlocked ? 256u * (uint32_t)(f & 1) + 4u * (uint32_t)(f >> 1) : 16u * kSRow * (uint32_t)f;
+    };
+
+    // This wave's A pieces: piece p = wave + 8 x is fragment p / 2, K half
+    // p % 2 (real when p < 2 F).
+    bool areal[kP];
+    uint32_t offA[kP], adst[kP], asrc[kP], araw[kP];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const int v = 2 * (kq >> 1) + (d & 1);
-        const int cl = c16 + 16 * (2 * (kq & 1) + (d >> 1));
-        adst[d] = areal ? &sm.a[0].v[wave][v][cl] : &sm.discard[d][lane];
+    for (int x = 0; x < kP; ++x) {
+        const int p = wave + 8 * x;
+        areal[x] = (x == 0 && F >= 4) || p < 2 * F;   // waves are 0..7
+        const int a = areal[x] ? p >> 1 : 0, h = p & 1;
+        offA[x] = (uint32_t)(m0 + 16 * a + c16) * row_bytes + 64u * h + 16u * kq;
+        adst[x] = (uint32_t)((a * 2 + h) * kKSteps) * kPieceBytes + 16u * lane;
+        // Its scales: staged row m0 + 16 a + c16 (blocked: relative to the
+        // first staged band), column 8 h + 2 kq.
+        const uint32_t ra = kBlocked ? (uint32_t)(m0 + 16 * a + c16) - (uint32_t)(m0 >> 7) * 128u
+                                     : (uint32_t)(16 * a + c16);
+        asrc[x] = kNvScaleOff + kSBBytes + sf_lds(ra, 8u * h + 2u * kq);
+        araw[x] = kNvRawOff + (uint32_t)(a * 2 + h) * kPieceBytes + 16u * lane;
     }
-    const uint32_t astep = areal ? (uint32_t)sizeof(AStage) : 0u;   // bytes from buffer 0 to buffer 1
 
     f4_t acc[F][kColFrags];
 
     {
         const int n = s_end - s_begin;
-        // Offsets of stage j of the chain, clamped to its last stage (loads
-        // past the chain re-read it, so every load is unconditional and in
-        // range).
+        // Stage j of the chain, clamped to its last stage (loads past the
+        // chain re-read it, so every load is unconditional and in range).
         auto sidx = [&](int j) { return s_begin + (j < n ? j : n - 1); };
-        auto sbyte = [&](int j) { return (uint32_t)__builtin_amdgcn_readfirstlane(sidx(j) * (kStageK / 2)); };
-        auto sscl = [&](int j) { return (uint32_t)__builtin_amdgcn_readfirstlane(sidx(j) * (int)kScaleStride); };
+        // Stage offset of the code loads of chain stage j for K half h.  In
+        // a 128-K last stage K half 1 has no codes: it re-reads bytes of its
+        // row (or of the next; none past the buffer), which its zero scales
+        // cancel.
+        const int half1_max = (int)row_bytes - kStageBytes > 0 ? (int)row_bytes - kStageBytes : 0;
+        auto soff = [&](int j, int h) {
+            const int o = sidx(j) * kStageBytes;
+            return (uint32_t)__builtin_amdgcn_readfirstlane(h == 1 && o > half1_max ? half1_max : o);
+        };
+        // LDS offset of the staged scales of stage j: its block, its part.
+        auto sblk = [&](int j) { return (uint32_t)((j >> 1) & 1) * kSBlockBytes + kPartStride * (uint32_t)(j & 1); };
+        auto lds_u16 = [&](uint32_t off) -> uint32_t { return *reinterpret_cast<const uint16_t*>(lds + off); };
+        // Whether chain stage j is a 128-K last stage, whose K half 1 gets
+        // zero scales (its codes are the next row's, or zeros past the
+        // buffer).
+        auto half_stage = [&](int j) { return half_last && sidx(j) == last_stage; };
 
-        // The scale bytes stay 8- and 16-bit values in the ring, so their
-        // zero extension happens where they are used, two stages after the
-        // load, not right after it (where it would wait for the load).
-        uint2 bq[2][kColFrags];
-        uint8_t bs[2][kColFrags];
-        i4_t aq[2];
-        uint16_t as[2];
-        const uint8_t* const sfa = ga.SFA;
-        const uint8_t* const sfb = ga.SFB;
-        auto load_b = [&](int slot, int j) {
-#pragma unroll
-            for (int f = 0; f < kColFrags; ++f) {
-                bq[slot][f] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rB, offB[f], sbyte(j), 0));
-                bs[slot][f] = sfb[sscl(j) + offSB[f]];
+        // ---- scale staging: block beta = stages 2 beta, 2 beta + 1, one
+        // 16-byte load per thread for each part (A: row-major waves 0-2).
+        const uint32_t band_bytes = (uint32_t)K * 8u;   // 128 rows x K/16 scales
+        i4_t stb, sta;
+        auto stage_load = [&](int beta) {
+            if constexpr (!kBlocked) {
+                // Two 8-byte loads, so that the second half of a 128-K last
+                // stage (past the row's scales) is read by none.
+                const int part = tid & 1, r = tid >> 1;
+                const int sg = sidx(2 * beta + part);
+                const bool hs = half_last && sg == last_stage;
+                auto load_row = [&](__amdgpu_buffer_rsrc_t rs, int row) {
+                    const uint32_t o = (uint32_t)row * row_scales + 16u * (uint32_t)sg;
+                    const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
+                    const uint2 hi =
+                        __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, hs ? kNoLoad : o + 8u, 0, 0));
+                    return i4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+                };
+                stb = load_row(rSB, n0 + r);
+                if (wave < 3) sta = load_row(rSA, m0 + r);
+            } else {
+                const int atom = tid >> 5, band = atom >> 3, part = (atom >> 2) & 1, quad = atom & 3;
+                const uint32_t sg = (uint32_t)sidx(2 * beta + part);
+                const uint32_t in_band = 512u * (4u * sg + (uint32_t)quad) + 16u * (uint32_t)(tid & 31);
+                stb = load16(rSB, (uint32_t)((n0 >> 7) + band) * band_bytes + in_band, 0);
+                sta = load16(rSA, (uint32_t)((m0 >> 7) + band) * band_bytes + in_band, 0);
             }
         };
-        auto load_as = [&](int j) -> uint16_t {
-            return *reinterpret_cast<const uint16_t*>(sfa + sscl(j) + offSA);
+        auto stage_store = [&](int beta) {
+            uint8_t* blk = lds + kNvScaleOff + (uint32_t)(beta & 1) * kSBlockBytes;
+            *reinterpret_cast<i4_t*>(blk + 16u * tid) = stb;
+            if (kBlocked || wave < 3) *reinterpret_cast<i4_t*>(blk + kSBBytes + 16u * tid) = sta;
         };
-        // Dequantises raw A (16 bytes, 2 scale bytes) into LDS buffer buf.
-        auto put_a = [&](int buf, const i4_t& q, uint16_t sc) {
-            const h2_t s2 = scales2(sc);
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-                *reinterpret_cast<h8_t*>(reinterpret_cast<char*>(adst[d]) + buf * astep) = dequant8((uint32_t)q[d], s2[d >> 1]);
+        // A scales of piece x for chain stage j, and B scale bytes of
+        // fragment f (zero for K half 1 of a 128-K last stage).
+        auto a_scales = [&](int x, int j) {
+            const uint32_t raw = lds_u16(asrc[x] + sblk(j));
+            return scales2(((wave & 1) != 0 && half_stage(j)) ? 0u : raw);
+        };
+        auto b_scale_bytes = [&](int f, int j) {
+            const uint32_t raw = lds_u16(sbsrc + sblk(j) + sfb_frag(f));
+            return (kh == 1 && half_stage(j)) ? 0u : raw;
         };
 
-        // Prologue: raw A of stage 0, then ring slot j (B of stage j, raw A
-        // of stage j + 1); stage 0 of A into LDS buffer 0.
+        i4_t bq[2][kColFrags];   // B codes of stages t, t + 1
+        h2_t scl[kColFrags];     // B scales of the current stage
+        h8_t bcur;               // the B operand of the next MFMAs
+        // Dword v of raw A codes q with scales s2 into A buffer buf.
+        auto put_a = [&](int buf, int x, uint32_t q, h2_t s2, int v) {
+            *reinterpret_cast<h8_t*>(lds + (uint32_t)buf * kABufBytes + adst[x] + (uint32_t)v * kPieceBytes) =
+                dequant8(q, s2[v >> 1]);
+        };
+
+        // Prologue: scale block 0 staged, block 1 loaded; B of stages 0, 1;
+        // A of stage 0 into buffer 0, raw A of stage 1 into the raw slots.
         {
-            const i4_t a0 = load16(rA, offA, sbyte(0));
-            const uint16_t s0 = load_as(0);
-            __builtin_amdgcn_sched_barrier(0);
+            // (Block 1's scales are loaded before the other loads, as in the
+            // loop, where B and A loads follow a block's.)
+            i4_t a0[kP], a1[kP];
+            stage_load(0);
+            i4_t st0b = stb, st0a = sta;
+            stage_load(1);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                load_b(j, j);
-                aq[j] = load16(rA, offA, sbyte(j + 1));
-                as[j] = load_as(j + 1);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int f = 0; f < kColFrags; ++f) bq[j][f] = load16(rB, offB[f], soff(j, kh));
+#pragma unroll
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) {
+                    a0[x] = load16(rA, offA[x], soff(0, wave & 1));
+                    a1[x] = load16(rA, offA[x], soff(1, wave & 1));
+                }
+            {
+                uint8_t* blk = lds + kNvScaleOff;
+                *reinterpret_cast<i4_t*>(blk + 16u * tid) = st0b;
+                if (kBlocked || wave < 3) *reinterpret_cast<i4_t*>(blk + kSBBytes + 16u * tid) = st0a;
             }
-            put_a(0, a0, s0);
+            lds_barrier();
+#pragma unroll
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) {
+                    const h2_t s2 = a_scales(x, 0);
+#pragma unroll
+                    for (int v = 0; v < kKSteps; ++v) put_a(0, x, (uint32_t)a0[x][v], s2, v);
+                    *reinterpret_cast<i4_t*>(lds + araw[x]) = a1[x];
+                }
+#pragma unroll
+            for (int f = 0; f < kColFrags; ++f) scl[f] = scales2(b_scale_bytes(f, 0));
+            bcur = dequant8((uint32_t)bq[0][0][0], scl[0][0]);
         }
 #pragma unroll
         for (int i = 0; i < F; ++i)
 #pragma unroll
             for (int f = 0; f < kColFrags; ++f) acc[i][f] = zero_acc();
-        pin_agprs<F>(acc);
+        pin_acc<F>(acc);
         lds_barrier();
 
         // Stage t at ring slot p = t % 2 (the loop below is unrolled by 2,
-        // so p is a compile-time constant and the stage has no branch).
+        // so p is a compile-time constant and the stage has no branch on it).
+        // The B operands are dequantised one MFMA group ahead: (fragment f,
+        // k-step v) during the MFMAs of the operand before it, (0, 0) of the
+        // next stage during those of (3, 3).
         auto stage = [&](auto parity, int t) {
             constexpr int p = decltype(parity)::value;
-            const AStage& ard = sm.a[p];
-            _Float16 sb[kColFrags];
+            const uint8_t* ard = lds + (uint32_t)p * kABufBytes + (uint32_t)(kh * kKSteps) * kPieceBytes + 16u * lane;
+            auto read_av = [&](int a, int v) {
+                return *reinterpret_cast<const h8_t*>(ard + (uint32_t)a * kAFragBytes + (uint32_t)v * kPieceBytes);
+            };
+            auto read_raw = [&](int x, int v) { return *reinterpret_cast<const uint32_t*>(lds + araw[x] + 4u * v); };
+            uint32_t snext[kColFrags];   // B scale bytes of stage t + 1
+            h2_t as2[kP];                // A scales of stage t + 1
+            uint32_t ar[kP];             // raw A of stage t + 1, dword of the current k-step
+            i4_t anext[kP];              // raw A of stage t + 2
+            h8_t av[F];                  // A operands of the current k-step
+            // Stage start: the A operands of k-step 0, the production's first
+            // raw dword and scales, the raw A of stage t + 2.
 #pragma unroll
-            for (int f = 0; f < kColFrags; ++f) sb[f] = scales2(bs[p][f])[0];
+            for (int a = 0; a < F; ++a) av[a] = read_av(a, 0);
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                const int v = 2 * kh + b;
-                // B operands of this k-step; after the second, the slot is
-                // re-loaded with stage t + 2.
-                h8_t bv[kColFrags];
-#pragma unroll
-                for (int f = 0; f < kColFrags; ++f) bv[f] = dequant8(b == 0 ? bq[p][f].x : bq[p][f].y, sb[f]);
-                if (b == 1) {
-#pragma unroll
-                    for (int f = 0; f < kColFrags; ++f) fence_after(bv[f]);
-                    load_b(p, t + 2);
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) {
+                    ar[x] = read_raw(x, 0);
+                    as2[x] = a_scales(x, t + 1);
+                    anext[x] = load16(rA, offA[x], soff(t + 2, wave & 1));
                 }
 #pragma unroll
-                for (int a = 0; a < F; ++a) {
-                    const h8_t av = ard.v[a][v][lane];
+            for (int v = 0; v < kKSteps; ++v) {
+                if (v == 2) {
 #pragma unroll
-                    for (int f = 0; f < kColFrags; ++f)
-                        acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[f], av, acc[a][f], 0, 0, 0);
+                    for (int f = 0; f < kColFrags; ++f) snext[f] = b_scale_bytes(f, t + 1);
                 }
-                if (b == 1) {
-                    // A of stage t + 1 -> the other buffer (its readers of
-                    // stage t - 1 passed the previous barrier), then the
-                    // slot's re-load with stage t + 3.
-                    put_a(p ^ 1, aq[p], as[p]);
-                    fence_after(aq[p]);
-                    aq[p] = load16(rA, offA, sbyte(t + 3));
-                    as[p] = load_as(t + 3);
-                }
-                // Issue order: the A operands read two fragments ahead of
-                // their MFMAs.
-                constexpr int kLead = F < 2 ? F : 2;
-                __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);   // LDS reads
+                // The MFMAs of k-step v, fragment-major; the B operand of the
+                // next group is dequantised during each group, and during
+                // the last group the A operands of k-step v + 1 are read into
+                // the registers each MFMA has just consumed.
+                if (v > 0) {
 #pragma unroll
-                for (int a = 0; a < F; ++a) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, kColFrags, 0);   // the MFMAs of fragment a
-                    if (a + kLead < F) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    for (int a = 0; a < F; ++a) av[a] = read_av(a, v);
+                }
+#pragma unroll
+                for (int f = 0; f < kColFrags; ++f) {
+#pragma unroll
+                    for (int a = 0; a < F; ++a) {
+                        acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bcur, av[a], acc[a][f], 0, 0, 0);
+                    }
+                    h8_t bnext;
+                    if (f + 1 < kColFrags) {
+                        bnext = dequant8((uint32_t)bq[p][f + 1][v], scl[f + 1][v >> 1]);
+                    } else if (v + 1 < kKSteps) {
+                        bnext = dequant8((uint32_t)bq[p][0][v + 1], scl[0][(v + 1) >> 1]);
+                    } else {
+#pragma unroll
+                        for (int g = 0; g < kColFrags; ++g) scl[g] = scales2(snext[g]);
+                        bnext = dequant8((uint32_t)bq[p ^ 1][0][0], scl[0][0]);
+                    }
+                    // A register of the ring whose last dword was just
+                    // dequantised is re-loaded with stage t + 2.
+                    const int done = f + 1 < kColFrags ? (v == kKSteps - 1 ? f + 1 : -1)
+                                                       : (v == kKSteps - 2 ? 0 : -1);
+                    if (done >= 0) {
+                        fence_after(bnext);
+                        bq[p][done] = load16(rB, offB[done], soff(t + 2, kh));
+                    }
+                    bcur = bnext;
+                }
+                // Dword v of the A pieces of stage t + 1 into the other
+                // buffer (its readers of stage t - 1 passed the last barrier);
+                // the next dword is read one k-step ahead.
+#pragma unroll
+                for (int x = 0; x < kP; ++x)
+                    if (areal[x]) {
+                        put_a(p ^ 1, x, ar[x], as2[x], v);
+                        if (v + 1 < kKSteps)
+                            ar[x] = read_raw(x, v + 1);
+                        else
+                            *reinterpret_cast<i4_t*>(lds + araw[x]) = anext[x];
+                    }
+                if (v == 1) {
+                    if constexpr (p == 0)
+                        stage_store((t >> 1) + 1);
+                    else
+                        stage_load((t >> 1) + 2);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-            pin_agprs<F>(acc);
+            pin_acc<F>(acc);
             lds_barrier();
         };
 
@@ -721,7 +848,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         for (; t + 1 < n; t += 2) pair_pass<0, 2>(stage, t);
         if (t < n) stage(Parity<0>{}, t);
     }
-    finish_segment<F, KH>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, cg, lane);
+    finish_segment<F, KH>(args, pos, first_chain, last_chain, lds, s_flag, acc, m0, n0, cg, lane);
 }
 
 // ------------------------------------------------------------------ MXFP4
@@ -731,14 +858,14 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 // N x K/32 bytes.  gfx950's block-scaled MFMA takes this form as it is:
 // v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands (format code 4)
 // multiplies each lane's 32 codes by that lane's E8M0 scale.  Lane (c16, kq)
-// supplies row c16 of an operand fragment and K = 32 kq .. 32 kq + 31 of the
-// 128-K step, which are bytes 16 kq .. 16 kq + 15 of the row's 64 bytes of
-// the stage, in the natural nibble order; its scale is byte 4 s + kq of the
-// row's scales at stage s.  No dequantisation, one MFMA per fragment pair
-// per stage.
+// supplies row c16 of an operand fragment and 32 K, here the 16 bytes
+// [64 kh + 16 kq, +16) of the row's stage bytes (K half kh of the stage, in
+// the natural nibble order), whose scale is byte 4 kh + kq of the row's 8
+// stage scale bytes.  No dequantisation: one MFMA per fragment pair per K
+// half of a stage.
 using v8i_t = int __attribute__((ext_vector_type(8)));
 
-__device__ __forceinline__ f4_t mfma_mx(i4_t b, uint8_t sb, i4_t a, uint32_t sa, f4_t c)
+__device__ __forceinline__ f4_t mfma_mx(i4_t b, uint32_t sb, i4_t a, uint32_t sa, f4_t c)
 {
     const v8i_t bv = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
     const v8i_t av = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
@@ -747,21 +874,24 @@ __device__ __forceinline__ f4_t mfma_mx(i4_t b, uint8_t sb, i4_t a, uint32_t sa,
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, 4, 4, 0, (int)sb, 0, (int)sa);
 }
 
-// One chain of an MXFP4 tile (same tile shape, K halves, schedule and end of
-// segment as run_segment):
-//   * B: each lane loads 16 bytes of its row per stage (the MFMA operand as
-//     it is) and its scale byte, two own stages ahead in a register ring.
-//   * A: wave cg of a K half loads fragments cg and cg + 4 of its half's
-//     next stage the same way and stores them with their scale bytes into
-//     the half's double-buffered LDS stage.
-//   * Per own stage each wave runs 4 F MFMAs of 16 x 16 x 128; one LDS-only
-//     barrier ends the stage pair.
+// One chain of an MXFP4 tile (same tile shape, stages, K halves, schedule
+// and end of segment as run_segment):
+//   * B: each lane loads its 16 bytes per fragment and stage (the MFMA
+//     operand as it is), two stages ahead in a register ring.
+//   * A: the waves copy the 2 F pieces of the next stage (fragment, K half)
+//     to LDS as they are, piece p by wave p % 8.
+//   * Scales: staged through LDS in blocks of two stages (8 bytes per row
+//     and stage), as in run_segment; each consumer reads its bytes there.
+//     A tile that ends with a 128-K stage gets zero scales and zero A codes
+//     for the missing half of that stage.
+//   * Per stage each wave runs 4 F MFMAs of 16 x 16 x 128; one LDS-only
+//     barrier ends the stage.
 template <int F, int KH>
 __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
-                                               bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
+                                               bool first_chain, bool last_chain, uint8_t* lds, int* s_flag)
 {
-    constexpr int kU = F > 4 ? 2 : 1;
     constexpr int kh = KH;
+    constexpr int kP = F > 4 ? 2 : 1;
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
@@ -774,42 +904,33 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 32;
+    const int last_stage = gs.stages - 1;
+    const bool half_last = (K % kStageK) != 0;
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
 
-    // Rows past M or N are beyond the buffers and read zeros.
-    uint32_t offB[kColFrags], offSB[kColFrags];
+    uint32_t offB[kColFrags];
 #pragma unroll
-    for (int f = 0; f < kColFrags; ++f) {
-        const uint32_t brow = (uint32_t)(n0 + 64 * cg + 16 * f + c16);
-        offB[f] = brow * row_bytes + 16u * kq;
-        offSB[f] = brow * row_scales + (uint32_t)kq;
-    }
-    uint32_t offA[kU], offSA[kU];
-    i4_t* vdst[kU];
-    uint32_t* sdst[kU];
-    uint32_t mstep[kU];
+    for (int f = 0; f < kColFrags; ++f)
+        offB[f] = (uint32_t)(n0 + 64 * cg + 16 * f + c16) * row_bytes + 64u * kh + 16u * kq;
+    const uint32_t sbsrc = kMxScaleOff + (uint32_t)(64 * cg + c16) * kMxSRow + 4u * kh + (uint32_t)kq;
+    const uint32_t sasrc = kMxScaleOff + kMxSBBytes + (uint32_t)c16 * kMxSRow + 4u * kh + (uint32_t)kq;
+
+    bool areal[kP];
+    bool ahalf1[kP];
+    uint32_t offA[kP], adst[kP];
 #pragma unroll
-    for (int x = 0; x < kU; ++x) {
-        const int a = cg + 4 * x;
-        const bool real = a < F;
-        const uint32_t arow = (uint32_t)(m0 + 16 * (real ? a : 0) + c16);
-        offA[x] = arow * row_bytes + 16u * kq;
-        offSA[x] = arow * row_scales + (uint32_t)kq;
-        // Stores of a unit past the tile's fragments go to the discard area,
-        // so the stage has no branch.
-        i4_t* disc = reinterpret_cast<i4_t*>(&sm.discard[0][0]);
-        vdst[x] = real ? &sm.mx[kh][0].v[a][lane] : disc + lane;
-        sdst[x] = real ? &sm.mx[kh][0].s[a][lane] : reinterpret_cast<uint32_t*>(disc + kWave) + lane;
-        mstep[x] = real ? (uint32_t)sizeof(MxStage) : 0u;
+    for (int x = 0; x < kP; ++x) {
+        const int p = wave + 8 * x;
+        areal[x] = (x == 0 && F >= 4) || p < 2 * F;   // waves are 0..7
+        const int a = areal[x] ? p >> 1 : 0, h = p & 1;
+        ahalf1[x] = h == 1;
+        offA[x] = (uint32_t)(m0 + 16 * a + c16) * row_bytes + 64u * h + 16u * kq;
+        adst[x] = (uint32_t)(a * 2 + h) * kPieceBytes + 16u * lane;
     }
-    auto put_a = [&](int buf, int x, i4_t v, uint8_t sc) {
-        *reinterpret_cast<i4_t*>(reinterpret_cast<char*>(vdst[x]) + buf * mstep[x]) = v;
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sdst[x]) + buf * mstep[x]) = sc;
-    };
 
     f4_t acc[F][kColFrags];
 #pragma unroll
@@ -819,82 +940,112 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
 
     {
         const int n = s_end - s_begin;
-        const int n_own = (n + 1 - kh) >> 1;
-        const int T = (n + 1) >> 1;
-        auto sidx = [&](int j) {
-            const int q = kh + 2 * j;
-            return s_begin + (q < n ? q : n - 1);
+        auto sidx = [&](int j) { return s_begin + (j < n ? j : n - 1); };
+        // As in run_segment: K half 1 of a 128-K last stage re-reads bytes
+        // of its row (its A codes are zeroed, its scales are zero).
+        const int half1_max = (int)row_bytes - kStageBytes > 0 ? (int)row_bytes - kStageBytes : 0;
+        auto soff = [&](int j, int h) {
+            const int o = sidx(j) * kStageBytes;
+            return (uint32_t)__builtin_amdgcn_readfirstlane(h == 1 && o > half1_max ? half1_max : o);
         };
-        auto sbyte = [&](int j) { return (uint32_t)__builtin_amdgcn_readfirstlane(sidx(j) * (kStageK / 2)); };
-        auto sscl = [&](int j) { return (uint32_t)__builtin_amdgcn_readfirstlane(sidx(j) * (kStageK / 32)); };
+        auto sblk = [&](int j) { return (uint32_t)((j >> 1) & 1) * kMxSBlockBytes + 8u * (uint32_t)(j & 1); };
+        auto lds_u8 = [&](uint32_t off) -> uint32_t { return lds[off]; };
 
-        // Scale bytes stay 8-bit in the ring: their zero extension happens
-        // at the MFMA that uses them, not right after the load.
-        i4_t bq[2][kColFrags], aq[2][kU];
-        uint8_t bs[2][kColFrags], as[2][kU];
+        // Scale staging: thread t loads the 8 scale bytes of stage t % 2 of
+        // B row t / 2 (and waves 0-2 of A row t / 2), as two 4-byte loads,
+        // so that the second half of a 128-K last stage (past the row's
+        // scales) is read by none.
+        uint2 stb, sta;
+        auto stage_load = [&](int beta) {
+            const int part = tid & 1, r = tid >> 1;
+            const int sg = sidx(2 * beta + part);
+            const bool hs = half_last && sg == last_stage;
+            auto load_row = [&](__amdgpu_buffer_rsrc_t rs, int row) {
+                const uint32_t o = (uint32_t)row * row_scales + 8u * (uint32_t)sg;
+                return uint2{__builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0),
+                             __builtin_amdgcn_raw_buffer_load_b32(rs, hs ? kNoLoad : o + 4u, 0, 0)};
+            };
+            stb = load_row(rSB, n0 + r);
+            if (wave < 3) sta = load_row(rSA, m0 + r);
+        };
+        auto stage_store = [&](int beta, uint2 vb, uint2 va) {
+            uint8_t* blk = lds + kMxScaleOff + (uint32_t)(beta & 1) * kMxSBlockBytes;
+            *reinterpret_cast<uint2*>(blk + 8u * tid) = vb;
+            if (wave < 3) *reinterpret_cast<uint2*>(blk + kMxSBBytes + 8u * tid) = va;
+        };
+
+        i4_t bq[2][kColFrags], aq[2][kP];
+        auto load_b = [&](int slot, int j) {
+#pragma unroll
+            for (int f = 0; f < kColFrags; ++f) bq[slot][f] = load16(rB, offB[f], soff(j, kh));
+        };
+        auto load_a = [&](int slot, int j) {
+#pragma unroll
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) aq[slot][x] = load16(rA, offA[x], soff(j, wave & 1));
+        };
+        // Raw A of chain stage j into buffer buf (zero codes for the missing
+        // half of a 128-K last stage).
+        auto put_a = [&](int buf, int x, i4_t q, int j) {
+            if (ahalf1[x] && half_last && sidx(j) == last_stage) q = i4_t{0, 0, 0, 0};
+            *reinterpret_cast<i4_t*>(lds + kMxABufBytes * (uint32_t)buf + adst[x]) = q;
+        };
         {
-            i4_t a0[kU];
-            uint8_t s0[kU];
+            // Scale block 0 and the raw A of stage 0 first, then the loads
+            // in the order two stages of the loop issue them (so the waits
+            // the compiler derives for the loop's first stage are those of
+            // every other).
+            i4_t a0[kP];
+            stage_load(0);
+            const uint2 st0b = stb, st0a = sta;
 #pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                a0[x] = load16(rA, offA[x], sbyte(0));
-                s0[x] = load_u8(rSA, offSA[x], sscl(0));
-            }
-            __builtin_amdgcn_sched_barrier(0);
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) a0[x] = load16(rA, offA[x], soff(0, wave & 1));
+            load_b(0, 0);
+            load_a(1, 1);
+            stage_load(1);
+            load_b(1, 1);
+            load_a(0, 2);
+            stage_store(0, st0b, st0a);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-#pragma unroll
-                for (int f = 0; f < kColFrags; ++f) {
-                    bq[j][f] = load16(rB, offB[f], sbyte(j));
-                    bs[j][f] = load_u8(rSB, offSB[f], sscl(j));
-                }
-#pragma unroll
-                for (int x = 0; x < kU; ++x) {
-                    aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
-                    as[j][x] = load_u8(rSA, offSA[x], sscl(j + 1));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int x = 0; x < kU; ++x) put_a(0, x, a0[x], s0[x]);
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) put_a(0, x, a0[x], 0);
         }
         lds_barrier();
 
         auto stage = [&](auto parity, int t) {
             constexpr int p = decltype(parity)::value;
-            const uint32_t sb2 = sbyte(t + 2), ss2 = sscl(t + 2);
-            const uint32_t sb3 = sbyte(t + 3), ss3 = sscl(t + 3);
+            uint32_t sb[kColFrags];
+#pragma unroll
+            for (int f = 0; f < kColFrags; ++f) sb[f] = lds_u8(sbsrc + sblk(t) + 16u * kMxSRow * f);
 #pragma unroll
             for (int a = 0; a < F; ++a) {
-                const i4_t av = sm.mx[kh][p].v[a][lane];
-                const uint32_t sa = sm.mx[kh][p].s[a][lane];
+                const i4_t av = *reinterpret_cast<const i4_t*>(lds + kMxABufBytes * (uint32_t)p +
+                                                               (uint32_t)(a * 2 + kh) * kPieceBytes + 16u * lane);
+                const uint32_t sa = lds_u8(sasrc + sblk(t) + 16u * kMxSRow * a);
 #pragma unroll
-                for (int f = 0; f < kColFrags; ++f) acc[a][f] = mfma_mx(bq[p][f], bs[p][f], av, sa, acc[a][f]);
+                for (int f = 0; f < kColFrags; ++f) acc[a][f] = mfma_mx(bq[p][f], sb[f], av, sa, acc[a][f]);
             }
             // A of stage t + 1 into the other buffer (its readers of stage
-            // t - 1 passed the previous barrier), then the ring slot's
-            // reloads: B of stage t + 2, A of stage t + 3.
+            // t - 1 passed the previous barrier), then the ring slots'
+            // re-loads: B of stage t + 2, A of stage t + 3.
 #pragma unroll
-            for (int x = 0; x < kU; ++x) put_a(p ^ 1, x, aq[p][x], as[p][x]);
-#pragma unroll
-            for (int f = 0; f < kColFrags; ++f) {
-                bq[p][f] = load16(rB, offB[f], sb2);
-                bs[p][f] = load_u8(rSB, offSB[f], ss2);
-            }
-#pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                aq[p][x] = load16(rA, offA[x], sb3);
-                as[p][x] = load_u8(rSA, offSA[x], ss3);
-            }
-            pin_agprs<F>(acc);
+            for (int x = 0; x < kP; ++x)
+                if (areal[x]) put_a(p ^ 1, x, aq[p ^ 1][x], t + 1);
+            load_b(p, t + 2);
+            load_a(p ^ 1, t + 3);
+            if constexpr (p == 0)
+                stage_store((t >> 1) + 1, stb, sta);
+            else
+                stage_load((t >> 1) + 2);
+            pin_acc<F>(acc);
             lds_barrier();
         };
         int t = 0;
-        for (; t + 1 < n_own; t += 2) pair_pass<0, 2>(stage, t);
-        if (t < n_own) stage(Parity<0>{}, t);
-        if (n_own < T) lds_barrier();
+        for (; t + 1 < n; t += 2) pair_pass<0, 2>(stage, t);
+        if (t < n) stage(Parity<0>{}, t);
     }
-    finish_segment<F, KH>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, cg, lane);
+    finish_segment<F, KH>(args, pos, first_chain, last_chain, lds, s_flag, acc, m0, n0, cg, lane);
 }
 
 // Wave-uniform values computed in vector registers (64-bit divisions have
@@ -925,19 +1076,19 @@ __device__ __forceinline__ Pos uniform(const Pos& p)
 // waves 4-7 half 1).  Both halves meet the same barriers in the same order.
 template <bool kMx, bool kBlocked, int F>
 __device__ __forceinline__ void run_chain(const LaunchArgs& args, const Pos& pos, int c0, int c1, bool first,
-                                          bool last, SharedMem& sm, int* s_flag)
+                                          bool last, uint8_t* lds, int* s_flag)
 {
     const bool half1 = __builtin_amdgcn_readfirstlane(opaque_tid() / kWave) >= kColGroups;
     if constexpr (kMx) {
         if (half1)
-            run_segment_mx<F, 1>(args, pos, c0, c1, first, last, sm, s_flag);
+            run_segment_mx<F, 1>(args, pos, c0, c1, first, last, lds, s_flag);
         else
-            run_segment_mx<F, 0>(args, pos, c0, c1, first, last, sm, s_flag);
+            run_segment_mx<F, 0>(args, pos, c0, c1, first, last, lds, s_flag);
     } else {
         if (half1)
-            run_segment<F, kBlocked, 1>(args, pos, c0, c1, first, last, sm, s_flag);
+            run_segment<F, kBlocked, 1>(args, pos, c0, c1, first, last, lds, s_flag);
         else
-            run_segment<F, kBlocked, 0>(args, pos, c0, c1, first, last, sm, s_flag);
+            run_segment<F, kBlocked, 0>(args, pos, c0, c1, first, last, lds, s_flag);
     }
 }
 
@@ -945,7 +1096,7 @@ __device__ __forceinline__ void run_chain(const LaunchArgs& args, const Pos& pos
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
 template <bool kMx, bool kBlocked>
-__device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
+__device__ __forceinline__ void walk_range(const LaunchArgs& args, uint8_t* lds, int* s_flag)
 {
     const int w = uniform(worker_id(args.G));
     const int64_t b1 = uniform(boundary(args.W, args.G, w + 1));
@@ -961,12 +1112,12 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
             const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
             const bool first = c0 == pos.stage, last = c1 == s_end;
             switch (pos.frags) {
-                case 1: run_chain<kMx, kBlocked, 1>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                case 2: run_chain<kMx, kBlocked, 2>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                case 3: run_chain<kMx, kBlocked, 3>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                case 4: run_chain<kMx, kBlocked, 4>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                case 5: run_chain<kMx, kBlocked, 5>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                default: run_chain<kMx, kBlocked, 6>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                case 1: run_chain<kMx, kBlocked, 1>(args, pos, c0, c1, first, last, lds, s_flag); break;
+                case 2: run_chain<kMx, kBlocked, 2>(args, pos, c0, c1, first, last, lds, s_flag); break;
+                case 3: run_chain<kMx, kBlocked, 3>(args, pos, c0, c1, first, last, lds, s_flag); break;
+                case 4: run_chain<kMx, kBlocked, 4>(args, pos, c0, c1, first, last, lds, s_flag); break;
+                case 5: run_chain<kMx, kBlocked, 5>(args, pos, c0, c1, first, last, lds, s_flag); break;
+                default: run_chain<kMx, kBlocked, 6>(args, pos, c0, c1, first, last, lds, s_flag); break;
             }
         }
         if (s_end < gs.stages) break;
@@ -974,38 +1125,26 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
     }
 }
 
-// The MFMA accumulators belong in AGPRs (the unified register file gives a
-// wave at two waves per SIMD 256 registers, VGPRs and AGPRs together).  The
-// compiler selects MFMAs with AGPR accumulators only in functions that may
-// use AGPRs; an AGPR operand of an empty asm statement marks the kernel so.
-__device__ __forceinline__ void use_agprs()
-{
-    asm volatile("; AGPR accumulators" ::"a"(0));
-}
-
 __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ SharedMem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     __shared__ int s_flag;
-    use_agprs();
-    walk_range<false, false>(args, sm, &s_flag);
+    walk_range<false, false>(args, lds, &s_flag);
 }
 
 // NVFP4 with the scales in the blocked layout.
 __global__ __launch_bounds__(kThreads) void nvfp4_blocked_sf_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ SharedMem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     __shared__ int s_flag;
-    use_agprs();
-    walk_range<false, true>(args, sm, &s_flag);
+    walk_range<false, true>(args, lds, &s_flag);
 }
 
 __global__ __launch_bounds__(kThreads) void mxfp4_group_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ SharedMem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
     __shared__ int s_flag;
-    use_agprs();
-    walk_range<true, false>(args, sm, &s_flag);
+    walk_range<true, false>(args, lds, &s_flag);
 }
 
 // Writes zeros to C of a group with K == 0 (the empty sum).
@@ -1158,7 +1297,7 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         for (const void* p : ops)
             if (!p || !aligned16(p))
                 return fail(NVFP4GG_INVALID_ARG, gs + "an operand pointer is NULL or not 16-byte aligned");
-        if (K[i] % kStageK != 0)
+        if (K[i] % (kStageK / 2) != 0)
             return fail(NVFP4GG_UNSUPPORTED, gs + "this kernel needs K % 128 == 0");
         // Byte offsets of the buffer loads are 32-bit and may run one tile
         // past the last row.

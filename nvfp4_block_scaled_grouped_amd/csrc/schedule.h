@@ -16,8 +16,9 @@
 //   * tile: (group, n-block, m-block); tiles are ordered by group, then
 //     n-block, then m-block, so the m-blocks that share a B strip are
 //     adjacent in the order.
-//   * stage: kStageK consecutive K of a tile.  A stage of a tile with f
-//     fragments costs unit_cost(f, fmt) units (about 10 ns of MI355X time
+//   * stage: kStageK consecutive K of a tile (a tile whose K is an odd
+//     multiple of 128 ends with a stage of 128 K).  A stage of a tile with
+//     f fragments costs unit_cost(f, fmt) units (about 10 ns of MI355X time
 //     each, fitted to measured stage times).  NVFP4 (fp16 MFMA after
 //     dequantisation): the B stream and its dequantisation do not grow with
 //     f, the MFMAs do.  MXFP4 (native FP4 MFMA, no dequantisation): a stage
@@ -43,16 +44,16 @@ namespace nvfp4sched {
 constexpr int kMaxFrags = 6;       // fragments per m-block
 constexpr int kFragRows = 16;      // rows per fragment
 constexpr int kTileN = 256;        // columns per n-block
-constexpr int kStageK = 128;       // K per stage
+constexpr int kStageK = 256;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
 constexpr int kTileCost = 250;     // cost units of a tile beyond its stages
-constexpr int kMaxUnitCost = 84;   // the costliest stage (NVFP4, 6 fragments)
+constexpr int kMaxUnitCost = 164;  // the costliest stage (NVFP4, 6 fragments)
 constexpr int kFmtNvfp4 = 0;       // E4M3 scale per 16 K, fp16 MFMA
 constexpr int kFmtMxfp4 = 1;       // E8M0 scale per 32 K, FP4 MFMA
 // Least cost handed to one workgroup: keeps every workgroup range longer
 // than the costliest stage, so the workgroups sharing a tile are
 // consecutive.
-constexpr int64_t kMinUnitsPerWG = 128;
+constexpr int64_t kMinUnitsPerWG = 256;
 static_assert(kMinUnitsPerWG >= kMaxUnitCost, "a workgroup range must hold a stage");
 
 struct GroupSched {
@@ -60,7 +61,7 @@ struct GroupSched {
     int frags;            // ceil(M / kFragRows)
     int mblocks;          // ceil(frags / maxf)
     int nblocks;          // ceil(N / kTileN)
-    int stages;           // K / kStageK
+    int stages;           // ceil(K / kStageK)
     int tile_begin;       // tiles before this group
     int fmt;              // kFmtNvfp4 or kFmtMxfp4 (selects the stage costs)
 };
@@ -68,7 +69,7 @@ struct GroupSched {
 NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
 // The schedule entry of a group with M, N >= 1 and K a positive multiple of
-// kStageK, in m-blocks of at most maxf (1..kMaxFrags) fragments.
+// 128, in m-blocks of at most maxf (1..kMaxFrags) fragments.
 NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin, int maxf = kMaxFrags,
                                      int fmt = kFmtNvfp4)
 {
@@ -79,7 +80,7 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
     g.frags = ceil_div_i(M, kFragRows);
     g.mblocks = ceil_div_i(g.frags, maxf);
     g.nblocks = ceil_div_i(N, kTileN);
-    g.stages = K / kStageK;
+    g.stages = ceil_div_i(K, kStageK);
     return g;
 }
 
@@ -88,8 +89,8 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 // dequantisation do not.  MXFP4: mostly the B stream.
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    if (fmt == kFmtMxfp4) return 60 + 2 * f;
-    return 24 + 10 * f;
+    if (fmt == kFmtMxfp4) return 80 + 4 * f;
+    return 20 + 24 * f;
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
