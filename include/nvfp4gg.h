@@ -31,7 +31,7 @@
  * workgroup) that the library allocates with hipMalloc on the first call for
  * a (device, stream) pair, sized for the device's compute units (no launch
  * has more workgroups), and keeps until the process ends: 3 partial tiles of
- * 96 KiB and one int per compute unit (72 MiB and 1 KiB on a 256-CU MI355X).
+ * 192 KiB and one int per compute unit (144 MiB and 1 KiB on a 256-CU MI355X).
  * Only that first call allocates (and is not capturable into a HIP graph);
  * every later call on the pair allocates, frees and synchronises nothing.
  * The counters return to zero at the end of every call, so calls on one
@@ -151,7 +151,7 @@ int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
  * Returns NVFP4GG_INVALID_ARG for a negative count. */
 int nvfp4_group_gemm_set_wait_limit(int polls);
 
-/* The m-block size, in fragments of 16 rows (1..6), used for every launch
+/* The m-block size, in fragments of 32 rows (1..6), used for every launch
  * (process-wide); 0 (the default) chooses it per launch from the problem
  * sizes.  Results do not depend on it beyond fp32 rounding order (each
  * output is one fp32 sum of exact products in every case); it exists for

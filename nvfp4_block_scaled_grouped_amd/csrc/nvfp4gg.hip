@@ -21,36 +21,32 @@
 //     (its scale operand contributes only a power of two, so it is passed
 //     1.0), then v_pk_mul_f16 multiplies by the E4M3 scale converted to fp16
 //     (exact: every E4M3 value is an fp16 value).
-//   * Tile: up to kMaxFrags fragments of 16 rows of A_i x 256 columns of B_i.  One
-//     workgroup of 8 waves per CU, two waves per SIMD.  Wave w owns the 64
-//     columns of column group w % 4 for all rows of the tile, and the 128-K
-//     stages of parity w / 4 (its K half): the two waves on a SIMD share the
-//     columns and split the stages, so each B element is loaded and
-//     dequantised once, by the wave that uses it, and the SIMD always has a
-//     second wave whose MFMAs cover this one's dequantisation (measured on
-//     MI355X: about two VALU operations per 16x16x32 MFMA run for free with
-//     two waves per SIMD, none with one).  A dequantised A operand read
-//     from LDS feeds 4 MFMAs (one per 16-column B fragment).
-//   * A: each K half dequantises its own stages of the tile's rows into a
-//     double-buffered LDS image in MFMA operand order (4 buffers of 32 KB).
-//     B: each lane loads 16 bytes of its row per stage (the four lanes of a
-//     row one 64-byte run) into a register ring two stages deep.
+//   * Tile: one workgroup of 8 waves per CU owns all rows of A_i (up to 192,
+//     in m-blocks of at most 6 fragments of 32 rows when M_i is larger) x 256
+//     columns of B_i, so every byte of B_i is streamed from memory once per
+//     m-block.  Wave w owns columns [32 w, 32 w + 32) for all rows of the
+//     tile over the whole K.  A is shared: each stage of the tile's A rows is
+//     dequantised once by the workgroup into LDS as fp16, already in MFMA
+//     operand order, and the waves read it with 16-byte LDS loads.  B is
+//     private to a wave: the four lanes of a B row load its 64 stage bytes as
+//     one contiguous run straight into registers (kept two stages ahead)
+//     and dequantise them there, so one dequantised B fragment feeds up to 12
+//     MFMAs.
 //   * K order: the sum over K is order-free.  A and B use the same order, so
 //     every pair (a_k, b_k) meets in the same MFMA slot; it is chosen so that
 //     each lane's 16 loaded bytes serve four k-steps.
-//   * Accumulation: per wave, one fp32 chain over its K half of a segment
-//     (at most 64 stages, 8192 K); the two halves are added through LDS at
-//     the end of the segment, segments and chains in fp32 after that.
+//   * Accumulation: one fp32 chain per output over at most 8192 K of a
+//     workgroup's segment; segments and chains are added in fp32 at the end.
 //   * Schedule: the work is the list of (tile, stage) units (schedule.h) with
-//     per-stage costs; a persistent grid of one workgroup per CU takes
-//     equal-cost contiguous ranges of it, so ragged groups fill the chip in
-//     one launch.  A tile whose stages span several workgroups is finished
-//     by the first of them (whose range carries the tile's fix-up cost): the
-//     others write their fp32 partial tiles to workspace slots and count
-//     themselves in on the tile's counter with a release; the first waits
-//     for them with acquires (bounded; on time-out it hands the fix-up over
-//     to the last to arrive), adds their partials to its own in workgroup
-//     order (deterministic) and writes C.
+//     measured per-stage costs; a persistent grid of one workgroup per CU
+//     takes equal-cost contiguous ranges of it, so ragged groups fill the
+//     chip in one launch.  A tile whose stages span several workgroups is
+//     finished by the first of them (whose range carries the tile's fix-up
+//     cost): the others write their fp32 partial tiles to workspace slots
+//     and count themselves in on the tile's counter; the first waits for
+//     them (bounded; on time-out it hands the fix-up over to the last to
+//     arrive), adds their partials to its own in workgroup order
+//     (deterministic) and writes C.
 //   * Loads are raw buffer loads whose range is the exact operand size, so
 //     rows past M_i or N_i read as zero without branches.
 #include <hip/hip_runtime.h>
@@ -81,55 +77,33 @@ typedef int i4_t __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;
 constexpr int kWaves = 8;                    // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
-constexpr int kColGroups = 4;                // waves per K half
-constexpr int kColFrags = kTileN / kColGroups / 16;   // 16-column B fragments per wave
-constexpr int kKSteps = kStageK / 2 / 32;    // MFMA k-steps of one K half of a stage (32 K each)
-constexpr int kStageBytes = kStageK / 2;     // bytes of a row per stage
-constexpr int kMaxChainStages = 64;          // stages of one chain (8192 K per K half)
-constexpr uint32_t kPieceBytes = kWave * 16; // one wave's 16 x 16 fp32 block
-// One fp32 partial tile: every (column group, fragment, column fragment)
-// piece at a fixed place, whatever the tile's fragment count.
-constexpr uint32_t kSlotBytes = kColGroups * kMaxFrags * kColFrags * kPieceBytes;
+constexpr int kKSteps = kStageK / 32;        // MFMA k-steps per stage (32 K each)
+constexpr int kMaxAFrags = 2 * kMaxFrags;    // 16-row A fragments of a tile
+constexpr int kMaxChainStages = 64;          // stages one fp32 chain accumulates (8192 K)
+constexpr int kSlotFloats = kWaves * kMaxAFrags * 2 * kWave * 4;   // one partial tile
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kCoherent = 16;                  // cache-policy bit sc1: device-scope coherent access
 constexpr int kWaitVmcnt0 = 0x0F70;            // s_waitcnt vmcnt(0) (expcnt, lgkmcnt not waited)
+// A partial-slot offset past the end of every workspace (the host checks
+// that the workspace stays below it): buffer loads there return zeros.
+constexpr uint32_t kNoSlot = 0xF0000000u;
 // Default bound on the first contributor's wait (polls of about a
 // microsecond each).
 constexpr int kWaitLimit = 1 << 20;
 
-static_assert(kColFrags == 4, "a wave owns 64 columns: four 16-column B fragments");
-static_assert(kKSteps == 4, "a K half of a stage is one 16-byte piece of 4 k-steps per lane");
-static_assert(kFragRows == 16, "fragments are the MFMA's 16 rows");
-static_assert(kMaxFrags == 6, "the kernels instantiate tiles of 1 to 6 fragments");
+// Issue-order hints that interleave the B dequantisation with the MFMAs of
+// each k-step (0 leaves the order to the compiler).
+#ifndef NVFP4_INTERLEAVE
+#define NVFP4_INTERLEAVE 1
+#endif
 
-// LDS of one workgroup (byte offsets).  NVFP4: two buffers of the
-// dequantised A of a stage, two blocks of staged scales (two stages of the
-// tile's B rows and A rows each), and the raw A codes of the next stage
-// (one slot per piece, each used by one wave only).  MXFP4: the same with raw A codes and
-// E8M0 scales.  At the end of a segment the first kRedBytes carry the
-// exchange of the two K halves' accumulators.
-constexpr uint32_t kAFragBytes = 2 * kKSteps * kWave * 16;        // [K half][k-step][lane] x 8 fp16
-constexpr uint32_t kABufBytes = kMaxFrags * kAFragBytes;          // 48 KB
-constexpr uint32_t kSRow = 2 * kStageK / 16;                      // E4M3 bytes of a row per block
-constexpr uint32_t kSBBytes = kTileN * kSRow;                     // also two 128-row bands of 8 atoms
-constexpr uint32_t kSABytes = kSBBytes;                           // the A rows' bands likewise
-constexpr uint32_t kSBlockBytes = kSBBytes + kSABytes;
-constexpr uint32_t kNvScaleOff = 2 * kABufBytes;
-constexpr uint32_t kNvRawOff = kNvScaleOff + 2 * kSBlockBytes;    // raw A of the next stage, one slot per piece
-constexpr uint32_t kNvLds = kNvRawOff + 2 * kMaxFrags * kPieceBytes;
+#ifndef NVFP4_XCD_REMAP
+#define NVFP4_XCD_REMAP 1
+#endif
 
-constexpr uint32_t kMxAFragBytes = 2 * kWave * 16;                // [K half][lane] x 32 codes
-constexpr uint32_t kMxABufBytes = kMaxFrags * kMxAFragBytes;
-constexpr uint32_t kMxSRow = 2 * kStageK / 32;                    // E8M0 bytes of a row per block
-constexpr uint32_t kMxSBBytes = kTileN * kMxSRow;
-constexpr uint32_t kMxSABytes = kMaxFrags * kFragRows * kMxSRow;
-constexpr uint32_t kMxSBlockBytes = kMxSBBytes + kMxSABytes;
-constexpr uint32_t kMxScaleOff = 2 * kMxABufBytes;
-constexpr uint32_t kMxLds = kMxScaleOff + 2 * kMxSBlockBytes;
-
-constexpr uint32_t kRedBytes = kColGroups * kMaxFrags * kColFrags * kPieceBytes;
-constexpr uint32_t kLdsBytes = kNvLds > kRedBytes ? (kNvLds > kMxLds ? kNvLds : kMxLds)
-                                                  : (kRedBytes > kMxLds ? kRedBytes : kMxLds);
-static_assert(kLdsBytes <= 160 * 1024, "the LDS of one workgroup fits a CU");
+static_assert(kTileN == kWaves * 32, "each wave owns two 16-column B fragments");
+static_assert(kMaxFrags == 6, "the kernel instantiates m-blocks of 1 to 6 fragments");
+static_assert(kKSteps == 4, "a stage is one 16-byte piece of 4 k-steps per lane");
 
 struct GroupArgs {
     const uint8_t* A;
@@ -144,18 +118,19 @@ struct GroupArgs {
 struct LaunchArgs {
     GroupSched sched[kMaxGroups];
     GroupArgs grp[kMaxGroups];
-    uint8_t* partials;    // kSlotsPerWG * G slots of kSlotBytes
+    float* partials;      // G * 2 slots of kSlotFloats
     int* counters;        // one per workgroup, zero between calls
     int64_t W;            // total cost
     int G;                // workgroups
     int ngroups;
+    int blocked_sf;       // scales in the blocked (128 x 4 atom) layout, else row-major
     int wait_limit;       // polls of a tile's first contributor waiting for the others
-    int pad;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferFlags);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             (int)kBufferFlags);
 }
 
 // Eight FP4 codes (one dword, nibble order) times a shared fp16 scale.
@@ -169,12 +144,6 @@ __device__ __forceinline__ h8_t dequant8(uint32_t packed, _Float16 s)
     return h8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
-// The two E4M3 scale bytes in the low 16 bits of a dword -> fp16.
-__device__ __forceinline__ h2_t scales2(uint32_t sc)
-{
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
-}
-
 // Four E4M3 scale bytes of a dword -> fp16.
 __device__ __forceinline__ void scales4(uint32_t sc, _Float16* out)
 {
@@ -186,17 +155,49 @@ __device__ __forceinline__ void scales4(uint32_t sc, _Float16* out)
     out[3] = s23.y;
 }
 
-// Buffer loads at voffset (per lane, range-checked) + soffset (wave-uniform,
-// in an SGPR, so per-stage offsets cost no vector registers).
+// Buffer loads at voffset (per lane) + soffset (wave-uniform, kept in an
+// SGPR so per-stage offsets cost no vector registers).
 __device__ __forceinline__ i4_t load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// A per-lane offset that is out of range of every buffer (operands are
-// smaller than 2 GiB): the load reads nothing and returns zeros.
-constexpr uint32_t kNoLoad = 0x80000000u;
 
+// LDS image of the dequantised A rows of one stage, in MFMA operand order:
+// [16-row fragment][k-step][lane] x 8 fp16 (48 KB).
+struct AStage {
+    h8_t v[kMaxAFrags][kKSteps][kWave];
+};
+
+// The workgroup's LDS: two A stages (dequantised fp16 for NVFP4, raw codes
+// for MXFP4).  At the end of a segment the same
+// memory carries the fp16 output tile on its way to C (rows padded by 16
+// bytes against bank conflicts).
+constexpr int kCTileStride = kTileN + 8;   // halves per LDS row of the output tile
+// MXFP4 kernel: the raw A codes of a stage in MFMA operand order (16 bytes
+// per lane per 16-row fragment) and each lane's E8M0 scale byte.
+struct MxStage {
+    i4_t v[kMaxAFrags][kWave];
+    uint32_t s[kMaxAFrags][kWave];
+};
+
+struct SharedMem {
+    union {
+        AStage a[2];
+        MxStage mx[2];
+        uint16_t ctile[kMaxFrags * kFragRows][kCTileStride];
+    };
+    // Target of the A pieces of waves with a unit past the tile's fragments
+    // (their writes are discarded), so the k-step needs no branch.
+    h8_t discard[kKSteps][kWave];
+    // Per-wave staging of the scale bytes of 4 stages (two blocks in
+    // flight): rows 0..31 are the wave's B rows, rows 32 + 16 x .. are its
+    // A unit x's rows; 8 dwords per row (4 stages x 8 scale bytes).  A wave
+    // loads a block with one 16-byte load per lane and redistributes it to
+    // the lanes that need each dword through its own rows of this array.
+    uint32_t sscr[2][kWaves][64][8];
+};
+static_assert(sizeof(SharedMem) <= 160 * 1024, "the LDS of one workgroup fits a CU");
 
 // fp16 round-to-nearest-even (overflow to inf) of 4 floats, packed.
 __device__ __forceinline__ uint2 pack4(f4_t v)
@@ -211,16 +212,11 @@ __device__ __forceinline__ uint2 pack4(f4_t v)
 
 // Workgroup barrier that hands LDS over between the waves: this wave's LDS
 // accesses complete before it, nobody's global loads are waited for (the
-// prefetched stages stay in flight), the asm's memory clobber keeps the
-// compiler from moving memory accesses across it, and the scheduling
-// barrier keeps it from moving any instruction across it (an instruction of
-// the next stage that consumed a just-issued load, moved up, would make the
-// wait before it drain the load ring).
+// prefetched stages stay in flight), and the asm's memory clobber keeps the
+// compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier()
 {
-    __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int P>
@@ -236,28 +232,102 @@ __device__ __forceinline__ int opaque_tid()
     return t;
 }
 
-__device__ __forceinline__ f4_t zero_acc() { return f4_t{0.0f, 0.0f, 0.0f, 0.0f}; }
-
-// Compiler fences: the asm takes the value as a register operand (so it is
-// computed before it) and clobbers memory (so no load or store moves across
-// it).  Placed before a register is re-loaded, it keeps the compiler from
-// copying a value whose load is still in flight.
-template <typename T>
-__device__ __forceinline__ void fence_after(const T& v)
+// A zero accumulator written by opaque moves, so the compiler does not keep
+// a zero constant alive across the persistent loop to copy from.
+__device__ __forceinline__ f4_t zero_acc()
 {
-    asm volatile("" ::"v"(v) : "memory");
+    f4_t z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float v;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(v));
+        z[e] = v;
+    }
+    return z;
 }
 
-// Keeps every accumulator in a register across a stage boundary (an empty
-// asm that reads and writes it), so the unrolled stages do not move
-// accumulators around between them.
-template <int F>
-__device__ __forceinline__ void pin_acc(f4_t (*acc)[4])
+// Piece (i, f) of the output tile, fp32 -> fp16 (round to nearest even,
+// overflow to inf), into the LDS copy of the tile.  Wave w holds B fragments
+// 2w, 2w + 1 (16 columns each): element r of lane (c16, kq) is tile row
+// 16 i + c16, tile column 32 w + 16 f + 4 kq + r.
+__device__ __forceinline__ void stage_c(SharedMem& sm, int i, int f, const f4_t& v, int wave, int lane)
+{
+    const int c16 = lane & 15, kq = lane >> 4;
+    *reinterpret_cast<uint2*>(&sm.ctile[16 * i + c16][32 * wave + 16 * f + 4 * kq]) = pack4(v);
+}
+
+// The LDS copy of the output tile to C, every global store 16 contiguous
+// bytes of a row.  Called by every thread of the workgroup once all pieces
+// are staged; the LDS is free on return.
+template <int MF>
+__device__ __forceinline__ void write_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0)
+{
+    const int tid = opaque_tid();
+    lds_barrier();
+    const int M = ga.M, N = ga.N;
+    const int rows = M - m0 < MF * kFragRows ? M - m0 : MF * kFragRows;
+    const int chunk = tid % (kTileN / 8);          // 8 columns = 16 bytes
+    const int n = n0 + 8 * chunk;
+    const bool vec_ok = (N & 7) == 0;
+    for (int r = tid / (kTileN / 8); r < rows; r += kThreads / (kTileN / 8)) {
+        if (n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(&sm.ctile[r][8 * chunk]);
+        uint16_t* dst = ga.C + (size_t)(m0 + r) * N + n;
+        if (vec_ok && n + 7 < N) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 8 && n + e < N; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+    lds_barrier();
+}
+
+// The output tile of the workgroup from the accumulators of its waves.
+template <int MF>
+__device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0,
+                                        const f4_t (*acc)[2], int wave)
+{
+    const int lane = opaque_tid() % kWave;
+#pragma unroll
+    for (int i = 0; i < 2 * MF; ++i)
+#pragma unroll
+        for (int f = 0; f < 2; ++f) stage_c(sm, i, f, acc[i][f], wave, lane);
+    write_c<MF>(sm, ga, m0, n0);
+}
+
+// One wave's fp32 block of a partial tile (2 MF x 2 x 4 floats per lane) at
+// base, in 1 KB lane-contiguous pieces.
+template <int MF>
+__device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t base, const f4_t (*acc)[2])
 {
 #pragma unroll
-    for (int a = 0; a < F; ++a)
+    for (int i = 0; i < 2 * MF; ++i)
 #pragma unroll
-        for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(acc[a][f]));
+        for (int f = 0; f < 2; ++f)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i4_t, acc[i][f]), r,
+                                                   base + (uint32_t)(2 * i + f) * (kWave * 16u), 0, kCoherent);
+}
+
+// acc += the block stored by store_block at base, kChunk pieces at a time
+// (the scheduling barrier keeps the loads of later chunks from being
+// hoisted, which bounds the registers in flight).
+template <int MF>
+__device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t base, f4_t (*acc)[2])
+{
+    constexpr int kPieces = 4 * MF;
+    constexpr int kChunk = 12;
+#pragma unroll
+    for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+        f4_t v[kChunk];
+#pragma unroll
+        for (int q = q0; q < q0 + kChunk && q < kPieces; ++q)
+            v[q - q0] = __builtin_bit_cast(
+                f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
+#pragma unroll
+        for (int q = q0; q < q0 + kChunk && q < kPieces; ++q) acc[q >> 1][q & 1] += v[q - q0];
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // The worker index of this workgroup.  Workgroups are dispatched round-robin
@@ -268,156 +338,95 @@ __device__ __forceinline__ void pin_acc(f4_t (*acc)[4])
 __device__ __forceinline__ int worker_id(int G)
 {
     const int b = blockIdx.x;
+#if NVFP4_XCD_REMAP
     if (G % kXcds == 0) return (b % kXcds) * (G / kXcds) + b / kXcds;
+#endif
     return b;
 }
 
-// ------------------------------------------------------ end of a segment
-//
-// Accumulators: acc[a][f] element r of lane (c16, kq) of the wave of column
-// group cg is tile row 16 a + c16, tile column 64 cg + 16 f + 4 kq + r.  Both
-// K halves hold a partial sum of the same (a, f) blocks.  The exchange
-// leaves the complete sum of fragment a in the K half that owns it: half 0
-// owns [0, Fh), half 1 [Fh, F) (Fh = ceil(F / 2)).  The K half KH is a
-// compile-time parameter of every function here (each wave runs the code
-// of its own half), so every loop bound and array index is a constant and
-// the accumulators stay in registers.
-
-// Byte offset of piece (cg, a, f) of lane `lane` in a partial-tile slot.
-__device__ __forceinline__ uint32_t piece_off(int cg, int a, int f, int lane)
+// Compiler fences: the asm takes the values as register operands (so they
+// are computed before it) and clobbers memory (so no load or store moves
+// across it).  Placed before a register is re-loaded, they keep the
+// compiler from copying a value whose load is still in flight.
+template <typename T>
+__device__ __forceinline__ void fence_after(const T& v)
 {
-    return (((uint32_t)(cg * kMaxFrags + a) * kColFrags + (uint32_t)f) * kWave + (uint32_t)lane) * 16u;
+    asm volatile("" ::"v"(v) : "memory");
 }
 
-// The fragments [lo, hi) that K half KH owns, and those of the other half.
-template <int F, int KH>
-struct Half {
-    static constexpr int Fh = (F + 1) / 2;
-    static constexpr int lo = KH == 0 ? 0 : Fh;
-    static constexpr int hi = KH == 0 ? Fh : F;
-    static constexpr int other_lo = KH == 0 ? Fh : 0;
-    static constexpr int other_hi = KH == 0 ? F : Fh;
-};
-
-template <int F, int KH>
-__device__ __forceinline__ void exchange_halves(uint8_t* lds, f4_t (*acc)[kColFrags], int cg, int lane)
+// The two E4M3 scale bytes at bits [shift, shift + 16) of a dword -> fp16.
+__device__ __forceinline__ h2_t scales2(uint32_t sc, uint32_t shift)
 {
-    using H = Half<F, KH>;
-#pragma unroll
-    for (int a = H::other_lo; a < H::other_hi; ++a)
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f) *reinterpret_cast<f4_t*>(lds + piece_off(cg, a, f, lane)) = acc[a][f];
-    lds_barrier();
-#pragma unroll
-    for (int a = H::lo; a < H::hi; ++a)
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f) acc[a][f] += *reinterpret_cast<const f4_t*>(lds + piece_off(cg, a, f, lane));
-    lds_barrier();   // the exchange area is the next segment's A stages
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc >> shift, 1.0f, false);
 }
 
-// This wave's owned pieces to a slot at base.
-template <int F, int KH>
-__device__ __forceinline__ void store_own(__amdgpu_buffer_rsrc_t r, uint32_t base, const f4_t (*acc)[kColFrags],
-                                          int cg, int lane)
+// Stages J .. L-1 of an unrolled pass: f(slot J % R, phase J % 4, i + J),
+// all of them, or (the tail) those below n.
+template <int J, int L, int R, class F>
+__device__ __forceinline__ void phase_pass(F& f, int i)
 {
-    using H = Half<F, KH>;
-#pragma unroll
-    for (int a = H::lo; a < H::hi; ++a)
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i4_t, acc[a][f]), r,
-                                                   base + piece_off(cg, a, f, lane), 0, 0);
-}
-
-// acc += the pieces stored by store_own at base (owned fragments only).
-template <int F, int KH>
-__device__ __forceinline__ void add_own(__amdgpu_buffer_rsrc_t r, uint32_t base, f4_t (*acc)[kColFrags], int cg,
-                                        int lane)
-{
-    using H = Half<F, KH>;
-#pragma unroll
-    for (int a = H::lo; a < H::hi; ++a) {
-        f4_t v[kColFrags];
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f)
-            v[f] = __builtin_bit_cast(
-                f4_t, __builtin_amdgcn_raw_buffer_load_b128(r, base + piece_off(cg, a, f, lane), 0, 0));
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f) acc[a][f] += v[f];
+    if constexpr (J < L) {
+        f(Parity<J % R>{}, Parity<J % 4>{}, i + J);
+        phase_pass<J + 1, L, R>(f, i);
     }
 }
 
-// The owned fragments of the output tile to C: fp32 -> fp16 (round to
-// nearest even, overflow to inf), four consecutive columns of one row per
-// lane, rows and columns past M, N skipped.
-template <int F, int KH>
-__device__ __forceinline__ void store_c(const GroupArgs& ga, int m0, int n0, const f4_t (*acc)[kColFrags], int cg,
-                                        int lane)
+template <int J, int L, int R, class F>
+__device__ __forceinline__ void phase_tail(F& f, int i, int n)
 {
-    using H = Half<F, KH>;
-    const int c16 = lane & 15, kq = lane >> 4;
-    const int M = ga.M, N = ga.N;
-    const bool vec = (N & 3) == 0;
-#pragma unroll
-    for (int a = H::lo; a < H::hi; ++a) {
-        const int row = m0 + 16 * a + c16;
-        if (row >= M) continue;
-        uint16_t* crow = ga.C + (size_t)row * N;
-#pragma unroll
-        for (int f = 0; f < kColFrags; ++f) {
-            const int col = n0 + 64 * cg + 16 * f + 4 * kq;
-            const uint2 w = pack4(acc[a][f]);
-            if (vec && col + 3 < N) {
-                *reinterpret_cast<uint2*>(crow + col) = w;
-            } else {
-                const uint16_t e0 = (uint16_t)w.x, e1 = (uint16_t)(w.x >> 16);
-                const uint16_t e2 = (uint16_t)w.y, e3 = (uint16_t)(w.y >> 16);
-                if (col < N) crow[col] = e0;
-                if (col + 1 < N) crow[col + 1] = e1;
-                if (col + 2 < N) crow[col + 2] = e2;
-                if (col + 3 < N) crow[col + 3] = e3;
-            }
+    if constexpr (J < L) {
+        if (i + J < n) {
+            f(Parity<J % R>{}, Parity<J % 4>{}, i + J);
+            phase_tail<J + 1, L, R>(f, i, n);
         }
     }
 }
 
-// The end of a segment: the two K halves meet in LDS; chains of one segment
-// meet in the scratch slot; the last chain finishes the tile alone, or as
-// one of several contributors (partial-tile store, counter, and the fix-up
-// by the tile's first contributor).
-template <int F, int KH>
+// The end of a segment: chains of one segment meet in the scratch slot; the
+// last chain finishes the tile alone, or as one of several contributors
+// (partial-tile store, counter, and the fix-up by the last to arrive).
+// acc holds the wave's part of the segment's sum: acc[i][f] element r of lane
+// (c16, kq) is tile row 16 i + c16, column 32 wave + 16 f + 4 kq + r.
+template <int MF>
 __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos& pos, bool first_chain,
-                                               bool last_chain, uint8_t* lds, int* s_flag,
-                                               f4_t (*acc)[kColFrags], int m0, int n0, int cg, int lane)
+                                               bool last_chain, SharedMem& sm, int* s_flag, f4_t (*acc)[2],
+                                               int m0, int n0, int wave)
 {
-    exchange_halves<F, KH>(lds, acc, cg, lane);
-
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
-    const __amdgpu_buffer_rsrc_t rP = make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotBytes);
-    const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
-    // Chains of one segment meet in the scratch slot (written and read by
-    // this workgroup only, in program order).
-    const uint32_t scratch = (uint32_t)scratch_slot(me) * kSlotBytes;
-    if (!first_chain) add_own<F, KH>(rP, scratch, acc, cg, lane);
+    const __amdgpu_buffer_rsrc_t rP =
+        make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
+    // Epilogue addresses, recomputed here rather than kept through the loop.
+    const uint32_t ewave_in_slot =
+        (uint32_t)wave * (kMaxAFrags * 2) * (kWave * 16u) + (uint32_t)(opaque_tid() % kWave) * 16u;
+    const uint32_t scratch_base =
+        (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + ewave_in_slot;
+    // Chains of one segment meet in the scratch slot.
+    if (!first_chain) load_block<MF>(rP, scratch_base, acc);
     if (!last_chain) {
-        store_own<F, KH>(rP, scratch, acc, cg, lane);
+        store_block<MF>(rP, scratch_base, acc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         return;
     }
 
-    // Finish the tile: alone, or as one of several contributors.
+    // Finish the tile: alone, or as one of several contributors.  Every
+    // wave holds its part of the segment's sum in acc.
     const int unit = pos.unit;
     const int64_t c_first = pos.tile_cost0;
     const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
     const int w_first = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_first));
     const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
     if (w_first == w_last) {
-        store_c<F, KH>(ga, m0, n0, acc, cg, lane);
+        asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
         return;
     }
+    const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
     int* counter = args.counters + counter_index(w_first);
-    auto slot_base = [&](int w) { return (uint32_t)partial_slot(w, w_last) * kSlotBytes; };
+    // Partial tile -> this workgroup's slot (partial_slot).
+    auto slot_base = [&](int w) {
+        return (uint32_t)partial_slot(w, w_last) * kSlotFloats * 4u + ewave_in_slot;
+    };
     // Who finishes the tile.  The first contributor's range ends with the
     // tile's first stages and carries the tile's start-up and wind-down cost
     // (kTileCost), so it should: it claims the fix-up and waits for the
@@ -429,20 +438,31 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     // finishes the tile: exactly one workgroup does, and nobody waits
     // unboundedly.
     //
-    // Memory ordering: every wave waits for its partial stores to complete
-    // (reach L2) before the workgroup barrier; thread 0 then publishes them
-    // with an agent-scope release add (the compiler writes L2 back first), and
-    // the finisher's thread 0 reads the counter with agent-scope acquire loads
-    // (the compiler invalidates this CU's caches after them) before the
-    // barrier after which its waves read the partials.
+    // Memory ordering.  Every value that passes between workgroups here (the
+    // partials and the counter) moves by agent-scope coherent accesses: the
+    // partial stores and loads carry the sc1 cache-policy bit, which is how
+    // gfx950 performs agent-scope relaxed atomic stores and loads (they write
+    // through to, and read from, the level that all XCDs share), and the
+    // counter operations are agent-scope atomics.  A contributor's waves wait
+    // until their partial stores have completed (s_waitcnt vmcnt(0)) before
+    // the workgroup barrier after which thread 0 adds to the counter, so the
+    // partials are in the shared level before the add is performed.  The
+    // finisher's thread 0 has the counter value back (the loop waits for it)
+    // before the barrier after which its waves issue their partial loads, so
+    // those loads are performed after the last add and read the stored
+    // values.  Release and acquire orderings would add what these accesses do
+    // not need: a write-back of the XCD's whole L2 before each add and an
+    // invalidation of it after each poll, which drops the B strips that the
+    // other workgroups of the XCD share (measured: up to 2x slower calls).
     const int others = w_last - w_first;
     bool fix;
     if (me != w_first) {
-        store_own<F, KH>(rP, slot_base(me), acc, cg, lane);
+        store_block<MF>(rP, slot_base(me), acc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         if (threadIdx.x == 0) {
-            const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            const int old =
+                __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             *s_flag = other_finishes(old, others) ? 1 : 0;
         }
         __syncthreads();
@@ -450,11 +470,13 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         __syncthreads();   // s_flag is reused below and by the next segment
     } else {
         if (threadIdx.x == 0) {
-            const int old = __hip_atomic_fetch_add(counter, kClaim, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+            const int old =
+                __hip_atomic_fetch_add(counter, kClaim, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             int done = first_finishes(old, others);
             for (int poll = 0; !done && poll < args.wait_limit; ++poll) {
                 __builtin_amdgcn_s_sleep(2);
-                done = first_finishes(__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT), others);
+                done = first_finishes(
+                    __hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), others);
             }
             *s_flag = done;
         }
@@ -462,12 +484,12 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
         __syncthreads();
         if (!fix) {
-            store_own<F, KH>(rP, slot_base(me), acc, cg, lane);
+            store_block<MF>(rP, slot_base(me), acc);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
             if (threadIdx.x == 0) {
-                const int old =
-                    __hip_atomic_fetch_add(counter, kHandOver - kClaim, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                const int old = __hip_atomic_fetch_add(counter, kHandOver - kClaim, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
                 *s_flag = first_finishes(old, others);   // the count completed meanwhile: still ours
             }
             __syncthreads();
@@ -477,43 +499,82 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     }
     if (!fix) return;
     // Sum the contributors' partials in workgroup order, so the result does
-    // not depend on who arrived last.
+    // not depend on who arrived last.  Loads carry the device-scope
+    // coherence bit; a contributor index past w_last gets an offset beyond
+    // the buffer, whose loads return zeros.
+    constexpr int kPieces = 4 * MF;
+    auto load_piece = [&](int w, int q) {
+        const uint32_t base = w <= w_last ? slot_base(w) : kNoSlot;
+        return __builtin_bit_cast(
+            f4_t, __builtin_amdgcn_raw_buffer_load_b128(rP, base + (uint32_t)q * (kWave * 16u), 0, kCoherent));
+    };
     if (me == w_first) {
-        // This workgroup's partial is still in registers (the first
-        // contributor ends its range with the tile's first stages, so it
-        // tends to finish last); the others are added to it.
-        for (int w = w_first + 1; w <= w_last; ++w) add_own<F, KH>(rP, slot_base(w), acc, cg, lane);
+        // This workgroup's partial is still in the accumulators (often the
+        // case: the first contributor ends its range with the tile's first
+        // stages, so it tends to finish last); the others are added to it,
+        // kChunk pieces of kBatch contributors in flight.  Tiles of 4 or more
+        // fragments take one contributor at a time (in two halves for 6
+        // fragments): their accumulators hold the registers.
+        constexpr int kChunk = MF <= 5 ? kPieces : kPieces / 2;
+        constexpr int kBatch = MF <= 3 ? 24 / kChunk : 1;
+        for (int w0 = w_first + 1; w0 <= w_last; w0 += kBatch) {
+#pragma unroll
+            for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+                f4_t v[kBatch][kChunk];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                        acc[(q0 + q) >> 1][(q0 + q) & 1] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("; fix-up, first contributor" ::: "memory");
+        store_c<MF>(sm, ga, m0, n0, acc, wave);
     } else {
-        // Every partial, this workgroup's own included, is read back.
-        using H = Half<F, KH>;
+        // Every partial, this workgroup's own included, is read back, so the
+        // accumulators are free: kChunk pieces of kBatch contributors in
+        // flight, each summed chunk straight to the LDS copy of the tile.
+        constexpr int kChunk = MF <= 3 ? kPieces : kPieces / 2;
+        constexpr int kBatch = (MF <= 2 ? 32 : 24) / kChunk;
+        const int flane = opaque_tid() % kWave;
 #pragma unroll
-        for (int a = H::lo; a < H::hi; ++a)
+        for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
+            f4_t sum[kChunk];
 #pragma unroll
-            for (int f = 0; f < kColFrags; ++f) acc[a][f] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int w = w_first; w <= w_last; ++w) add_own<F, KH>(rP, slot_base(w), acc, cg, lane);
+            for (int q = 0; q < kChunk; ++q) sum[q] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int w0 = w_first; w0 <= w_last; w0 += kBatch) {
+                f4_t v[kBatch][kChunk];
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) v[b][q] = load_piece(w0 + b, q0 + q);
+#pragma unroll
+                for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+                    for (int q = 0; q < kChunk && q0 + q < kPieces; ++q) sum[q] += v[b][q];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int q = 0; q < kChunk && q0 + q < kPieces; ++q)
+                stage_c(sm, (q0 + q) >> 1, (q0 + q) & 1, sum[q], wave, flane);
+        }
+        asm volatile("; fix-up" ::: "memory");
+        write_c<MF>(sm, ga, m0, n0);
     }
-    store_c<F, KH>(ga, m0, n0, acc, cg, lane);
-    if (threadIdx.x == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stages J .. L-1 of an unrolled pass: f(Parity<J % 2>, i + J).
-template <int J, int L, class Fn>
-__device__ __forceinline__ void pair_pass(Fn& f, int i)
-{
-    if constexpr (J < L) {
-        f(Parity<J % 2>{}, i + J);
-        pair_pass<J + 1, L>(f, i);
-    }
-}
 
-// --------------------------------------------------------------- NVFP4
-//
-// One chain [s_begin, s_end) of the stages of a tile with F fragments: a
+// One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
-// stages; first_chain / last_chain place this chain in its segment.  A stage
-// is 256 K: 128 bytes of every A and B row and 16 scale bytes.  All 8 waves
-// work on the same stage; K half kh of a stage is its row bytes
-// [64 kh, 64 kh + 64), run by the 4 waves of half kh as 4 k-steps.
+// stages (one chain for any K <= 8192); first_chain / last_chain place this
+// chain in its segment.
 //
 // MFMA: v_mfma_f32_16x16x32_f16 with B as the first operand (16 columns of
 // B_i) and A as the second (16 rows of A_i).  Lane (c16, kq) = (lane % 16,
@@ -521,334 +582,295 @@ __device__ __forceinline__ void pair_pass(Fn& f, int i)
 // 4 kq .. 4 kq + 3 of the first operand's side, i.e. output row c16 and
 // output columns 4 kq .. 4 kq + 3 of the 16 x 16 block.
 //
-// K order within a K half (the sum is order-free; A and B use the same
-// order): at k-step v lane (c16, kq) holds dword v of the 16 bytes
-// [64 kh + 16 kq, +16) of its row's stage bytes, whose scale is byte
-// 8 kh + 2 kq + v / 2 of the row's 16 stage scale bytes.  So every lane
-// loads 16 contiguous bytes of B per fragment and stage, the four lanes of
-// a row one 64-byte run.
+// Waves: wave w owns columns [32 w, 32 w + 32) of the tile (B fragments
+// f = 0, 1 of 16 columns) for all 2 MF 16-row A fragments, over the whole K
+// of the chain, so every byte of B is loaded and dequantised once per tile,
+// by one wave, and one dequantised B fragment feeds 2 MF MFMAs.
 //
-// A: the 2 F pieces of a stage (fragment a, K half h: 16 rows x 64 bytes)
-// are dequantised by the waves, piece p by wave p % 8; lane (c16, kq) of it
-// loads the same 16 bytes that consumer lane (c16, kq) of K half h needs
-// and writes dword v, dequantised, as that lane's operand of k-step v.
+// K order within a stage (128 K, 64 bytes of a row; the sum is order-free
+// and A and B use the same order): at k-step v lane (c16, kq) holds the 8
+// codes at K 32 kq + 8 v, i.e. dword v of the 16 bytes [16 kq, +16) of the
+// row's stage bytes, whose scale block is 2 kq + v / 2 (scale bytes
+// 2 (kq % 2), + 1 of dword kq / 2 of the row's 8 stage scale bytes).  So the
+// four lanes of a row read its 64 stage bytes as one contiguous run, and
+// one 16-byte load per B fragment and stage feeds all four k-steps.
 //
-// Scales: the scale bytes of a block of two stages of the tile's B rows and
-// A rows are loaded by all threads (16 contiguous bytes per thread), one
-// stage later written to one of two LDS blocks, and read from there: B's by
-// their consumers, A's by the producers.  A tile that ends with a 128-K
-// stage gets zero scales for the missing half of that stage, so its codes
-// (the next row's, or zeros past the buffer) contribute exact zeros.
+// A: each stage of the tile's 2 MF fragments of 16 rows is dequantised once
+// by the workgroup into LDS, in operand order.  Fragment a belongs to wave
+// a % 8 (its unit a / 8), so a wave has at most two units.
 //
-// Pipeline, per stage t of the chain (register ring slot p = t % 2):
-//   * B of stage t is in bq[p] (loaded two stages earlier).  The B operands
-//     of a k-step are dequantised during the MFMAs of the previous one
-//     (those of k-step 0 during k-step 3 of the stage before); the slot is
-//     re-loaded with stage t + 2 once its last dword is dequantised.
-//   * A of stage t is in LDS buffer p.  The raw A of stage t + 1 (in the
-//     wave's raw LDS slot) is dequantised into the other buffer, one dword
-//     per k-step; the raw A of stage t + 2, loaded at the start of the
-//     stage, replaces it in the slot at the end.
-//   * Scale block b (stages 2 b, 2 b + 1) is loaded during stage 2 b - 3
-//     and written during stage 2 b - 2 into LDS block b % 2; it is read
-//     from stage 2 b - 1 on (the B look-ahead and the A production read the
-//     next stage's scales), and block b - 2 was last read in stage 2 b - 4.
+// Pipeline, per stage i of the chain (register ring slot p = i % kRing):
+//   * B of stage i is in bq[p], bs[p] (loaded kRing stages earlier); it is
+//     re-loaded with stage i + kRing once its last k-step is dequantised.
+//   * A of stage i is in LDS buffer i % 2.  The raw A of stage i + 1 (aq[p],
+//     as[p], loaded kRing stages earlier) is dequantised into the other
+//     buffer, one piece per k-step of the MFMA loop, then re-loaded with
+//     stage i + 1 + kRing.
 //   * One LDS-only barrier ends the stage.
-template <int F, bool kBlocked, int KH>
+template <int MF, bool kBlocked>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
-                                            bool first_chain, bool last_chain, uint8_t* lds, int* s_flag)
+                                            bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
-    constexpr int kh = KH;
-    constexpr int kP = F > 4 ? 2 : 1;   // A pieces per wave: pieces w and w + 8 of 2 F
+    constexpr int NA = 2 * MF;   // 16-row A fragments
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int cg = wave & 3;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int lane = tid % kWave;
-    const int c16 = lane & 15, kq = lane >> 4;
+    const int c16 = lane & 15;
+    const int kq = lane >> 4;
     const int M = ga.M, N = ga.N, K = ga.K;
     const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 16;
-    const int last_stage = gs.stages - 1;
-    const bool half_last = (K % kStageK) != 0;   // the tile's last stage holds 128 K
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
-    // Blocked scale arrays hold whole 128-row bands.
-    const uint32_t sa_rows = kBlocked ? (uint32_t)(M + 127) / 128u * 128u : (uint32_t)M;
-    const uint32_t sb_rows = kBlocked ? (uint32_t)(N + 127) / 128u * 128u : (uint32_t)N;
-    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, sa_rows * row_scales);
-    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, sb_rows * row_scales);
+    // Blocked scales: rows padded to a multiple of 128 (the layout's atoms
+    // are 128 rows x 4 scales; K / 16 is a multiple of 8 here).
+    constexpr bool blocked = kBlocked;
+    const uint32_t sf_rows_a = blocked ? (uint32_t)(M + 127) & ~127u : (uint32_t)M;
+    const uint32_t sf_rows_b = blocked ? (uint32_t)(N + 127) & ~127u : (uint32_t)N;
+    const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, sf_rows_a * row_scales);
+    const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, sf_rows_b * row_scales);
+    const uint32_t sshift = 16u * (uint32_t)(kq & 1);   // this lane's scale bytes within a dword
 
-    // B operand of lane (c16, kq) in fragment f: row n0 + 64 cg + 16 f + c16
-    // (rows past N read 0), bytes [64 kh + 16 kq, +16) of each stage.
-    uint32_t offB[kColFrags];
+    // B operand of lane (c16, kq) in fragment f: row n0 + 32 wave + 16 f + c16
+    // (rows past N read 0).
+    uint32_t offB[2];
 #pragma unroll
-    for (int f = 0; f < kColFrags; ++f)
-        offB[f] = (uint32_t)(n0 + 64 * cg + 16 * f + c16) * row_bytes + 64u * kh + 16u * kq;
-    // Staged scales (both layouts: thread t copies 16 bytes to byte 16 t of
-    // the block's B part, and of its A part).  Row-major: the B part is
-    // [row][32 bytes], the row's 16 scale bytes of each of the two stages;
-    // the A part likewise for the tile's rows.  Blocked: the B part is the
-    // two 128-row bands of the tile's B rows, 8 atoms of 512 bytes each (4
-    // scale columns of 128 rows; the 4 atoms of a stage in column order,
-    // stage 0 first); the A part the same for the two bands from the one
-    // holding row m0.  Byte offset of (row r, scale column c of stage part
-    // q) in a part:
-    //   row-major: 32 r + 16 q + c
-    //   blocked:   512 (8 (r / 128) + 4 q + c / 4) + 16 (r % 32) + 4 ((r / 32) % 4) + c % 4
-    auto sf_lds = [&](uint32_t r, uint32_t c) -> uint32_t {
-        return kBlocked ? 512u * (8u * (r >> 7) + (c >> 2)) + 16u * (r & 31u) + 4u * ((r >> 5) & 3u) + (c & 3u)
-                        : kSRow * r + c;
-    };
-    constexpr uint32_t kPartStride = kBlocked ? 2048u : 16u;   // stage part 1 of a block
-    // This lane's B scales: tile row 64 cg + 16 f + c16, column 8 kh + 2 kq
-    // (two bytes: k-steps 0-1 and 2-3).  Fragment f adds sfb_frag(f).
-    const uint32_t sbsrc = kNvScaleOff + sf_lds((uint32_t)(64 * cg + c16), 8u * kh + 2u * kq);
-    auto sfb_frag = [&](int f) -> uint32_t {
-        return kBlocked ? 256u * (uint32_t)(f & 1) + 4u * (uint32_t)(f >> 1) : 16u * kSRow * (uint32_t)f;
-    };
-
-    // This wave's A pieces: piece p = wave + 8 x is fragment p / 2, K half
-    // p % 2 (real when p < 2 F).
-    bool areal[kP];
-    uint32_t offA[kP], adst[kP], asrc[kP], araw[kP];
-#pragma unroll
-    for (int x = 0; x < kP; ++x) {
-        const int p = wave + 8 * x;
-        areal[x] = (x == 0 && F >= 4) || p < 2 * F;   // waves are 0..7
-        const int a = areal[x] ? p >> 1 : 0, h = p & 1;
-        offA[x] = (uint32_t)(m0 + 16 * a + c16) * row_bytes + 64u * h + 16u * kq;
-        adst[x] = (uint32_t)((a * 2 + h) * kKSteps) * kPieceBytes + 16u * lane;
-        // Its scales: staged row m0 + 16 a + c16 (blocked: relative to the
-        // first staged band), column 8 h + 2 kq.
-        const uint32_t ra = kBlocked ? (uint32_t)(m0 + 16 * a + c16) - (uint32_t)(m0 >> 7) * 128u
-                                     : (uint32_t)(16 * a + c16);
-        asrc[x] = kNvScaleOff + kSBBytes + sf_lds(ra, 8u * h + 2u * kq);
-        araw[x] = kNvRawOff + (uint32_t)(a * 2 + h) * kPieceBytes + 16u * lane;
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
+        offB[f] = brow * row_bytes + 16u * kq;
     }
 
-    f4_t acc[F][kColFrags];
+    // This wave's A units: kU = 1 for MF <= 4, else 2 (unit x is fragment
+    // a = w + 8 x).  A unit past the tile's fragments (a >= 2 MF) loads the
+    // rows of fragment a % (2 MF) again (cache hits) and writes the discard
+    // area.
+    constexpr int kU = NA > kWaves ? 2 : 1;
+    // Register ring depth: stage i's loads go out kRing stages ahead.
+    // (Measured on MI355X: rings of 1, 2 and 4 stages time the same; the
+    // stage is bound by its issue, not by the load latency.)
+    constexpr int kRing = 2;
+    static_assert(4 % kRing == 0, "the ring depth divides the 4-stage scale block");
+    uint32_t offA[2];
+    h8_t* adst[2];          // k-step 0 of the unit's fragment in LDS buffer 0
+    uint32_t abuf_step[2];  // bytes from buffer 0 to buffer 1 (0 for the discard area)
+#pragma unroll
+    for (int x = 0; x < kU; ++x) {
+        const int a = wave + kWaves * x;
+        const bool real = a < NA;
+        const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);   // rows past M read 0
+        offA[x] = arow * row_bytes + 16u * kq;
+        adst[x] = real ? &sm.a[0].v[a][0][lane] : &sm.discard[0][lane];
+        abuf_step[x] = real ? (uint32_t)sizeof(AStage) : 0u;
+    }
+
+    f4_t acc[NA][2];
 
     {
         const int n = s_end - s_begin;
-        // Stage j of the chain, clamped to its last stage (loads past the
-        // chain re-read it, so every load is unconditional and in range).
-        auto sidx = [&](int j) { return s_begin + (j < n ? j : n - 1); };
-        // Stage offset of the code loads of chain stage j for K half h.  In
-        // a 128-K last stage K half 1 has no codes: it re-reads bytes of its
-        // row (or of the next; none past the buffer), which its zero scales
-        // cancel.
-        const int half1_max = (int)row_bytes - kStageBytes > 0 ? (int)row_bytes - kStageBytes : 0;
-        auto soff = [&](int j, int h) {
-            const int o = sidx(j) * kStageBytes;
-            return (uint32_t)__builtin_amdgcn_readfirstlane(h == 1 && o > half1_max ? half1_max : o);
-        };
-        // LDS offset of the staged scales of stage j: its block, its part.
-        auto sblk = [&](int j) { return (uint32_t)((j >> 1) & 1) * kSBlockBytes + kPartStride * (uint32_t)(j & 1); };
-        auto lds_u16 = [&](uint32_t off) -> uint32_t { return *reinterpret_cast<const uint16_t*>(lds + off); };
-        // Whether chain stage j is a 128-K last stage, whose K half 1 gets
-        // zero scales (its codes are the next row's, or zeros past the
-        // buffer).
-        auto half_stage = [&](int j) { return half_last && sidx(j) == last_stage; };
-
-        // ---- scale staging: block beta = stages 2 beta, 2 beta + 1, one
-        // 16-byte load per thread for each part (A: row-major waves 0-2).
-        const uint32_t band_bytes = (uint32_t)K * 8u;   // 128 rows x K/16 scales
-        i4_t stb, sta;
-        auto stage_load = [&](int beta) {
-            if constexpr (!kBlocked) {
-                // Two 8-byte loads, so that the second half of a 128-K last
-                // stage (past the row's scales) is read by none.
-                const int part = tid & 1, r = tid >> 1;
-                const int sg = sidx(2 * beta + part);
-                const bool hs = half_last && sg == last_stage;
-                auto load_row = [&](__amdgpu_buffer_rsrc_t rs, int row) {
-                    const uint32_t o = (uint32_t)row * row_scales + 16u * (uint32_t)sg;
-                    const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0));
-                    const uint2 hi =
-                        __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, hs ? kNoLoad : o + 8u, 0, 0));
-                    return i4_t{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-                };
-                stb = load_row(rSB, n0 + r);
-                if (wave < 3) sta = load_row(rSA, m0 + r);
-            } else {
-                const int atom = tid >> 5, band = atom >> 3, part = (atom >> 2) & 1, quad = atom & 3;
-                const uint32_t sg = (uint32_t)sidx(2 * beta + part);
-                const uint32_t in_band = 512u * (4u * sg + (uint32_t)quad) + 16u * (uint32_t)(tid & 31);
-                stb = load16(rSB, (uint32_t)((n0 >> 7) + band) * band_bytes + in_band, 0);
-                sta = load16(rSA, (uint32_t)((m0 >> 7) + band) * band_bytes + in_band, 0);
-            }
-        };
-        auto stage_store = [&](int beta) {
-            uint8_t* blk = lds + kNvScaleOff + (uint32_t)(beta & 1) * kSBlockBytes;
-            *reinterpret_cast<i4_t*>(blk + 16u * tid) = stb;
-            if (kBlocked || wave < 3) *reinterpret_cast<i4_t*>(blk + kSBBytes + 16u * tid) = sta;
-        };
-        // A scales of piece x for chain stage j, and B scale bytes of
-        // fragment f (zero for K half 1 of a 128-K last stage).
-        auto a_scales = [&](int x, int j) {
-            const uint32_t raw = lds_u16(asrc[x] + sblk(j));
-            return scales2(((wave & 1) != 0 && half_stage(j)) ? 0u : raw);
-        };
-        auto b_scale_bytes = [&](int f, int j) {
-            const uint32_t raw = lds_u16(sbsrc + sblk(j) + sfb_frag(f));
-            return (kh == 1 && half_stage(j)) ? 0u : raw;
+        // Stage offsets (wave-uniform, in SGPRs); stages past the chain
+        // re-read its last stage, so every load is unconditional and in range.
+        auto sbyte = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
         };
 
-        i4_t bq[2][kColFrags];   // B codes of stages t, t + 1
-        h2_t scl[kColFrags];     // B scales of the current stage
-        h8_t bcur;               // the B operand of the next MFMAs
-        // Dword v of raw A codes q with scales s2 into A buffer buf.
-        auto put_a = [&](int buf, int x, uint32_t q, h2_t s2, int v) {
-            *reinterpret_cast<h8_t*>(lds + (uint32_t)buf * kABufBytes + adst[x] + (uint32_t)v * kPieceBytes) =
-                dequant8(q, s2[v >> 1]);
-        };
+        i4_t bq[kRing][2];
+        i4_t aq[kRing][2];
 
-        // Prologue: scale block 0 staged, block 1 loaded; B of stages 0, 1;
-        // A of stage 0 into buffer 0, raw A of stage 1 into the raw slots.
-        {
-            // (Block 1's scales are loaded before the other loads, as in the
-            // loop, where B and A loads follow a block's.)
-            i4_t a0[kP], a1[kP];
-            stage_load(0);
-            i4_t st0b = stb, st0a = sta;
-            stage_load(1);
+        // Scale staging: lane L loads 16 bytes (2 stages) of the scale row
+        // L / 2 of the wave (B rows, then each A unit's 16 rows) for a block of
+        // 4 stages, and writes them to its rows of sm.sscr.  Only the wave
+        // itself reads its rows, and a wave's LDS accesses complete in issue
+        // order, so no barrier guards them.  A block that runs past the end
+        // of K reads the next row's bytes or, past the buffer, zeros; the
+        // stages that would use them do not exist.
+        //
+        // Row-major scales: the 16 bytes are contiguous.  Blocked scales
+        // (the 128 x 4 atom layout): scale column c of row r is byte
+        // 512 ((r / 128) (K / 64) + c / 4) + 16 (r % 32) + 4 ((r / 32) % 4)
+        // + c % 4, so the 16 bytes are four 4-byte runs (scale columns
+        // 4q .. 4q + 3 of consecutive atoms), 512 bytes apart.
+        const int slane = lane;
+        auto sf_off = [&](int r) {
+            return blocked ? (uint32_t)(r >> 7) * (uint32_t)K * 8u + (uint32_t)(r & 31) * 16u +
+                                 (uint32_t)((r >> 5) & 3) * 4u + 2048u * (slane & 1)
+                           : (uint32_t)r * row_scales + 16u * (slane & 1);
+        };
+        const uint32_t offSBs = sf_off(n0 + 32 * wave + (slane >> 1));
+        uint32_t offSAs[2];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int f = 0; f < kColFrags; ++f) bq[j][f] = load16(rB, offB[f], soff(j, kh));
-#pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) {
-                    a0[x] = load16(rA, offA[x], soff(0, wave & 1));
-                    a1[x] = load16(rA, offA[x], soff(1, wave & 1));
-                }
-            {
-                uint8_t* blk = lds + kNvScaleOff;
-                *reinterpret_cast<i4_t*>(blk + 16u * tid) = st0b;
-                if (kBlocked || wave < 3) *reinterpret_cast<i4_t*>(blk + kSBBytes + 16u * tid) = st0a;
-            }
-            lds_barrier();
-#pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) {
-                    const h2_t s2 = a_scales(x, 0);
-#pragma unroll
-                    for (int v = 0; v < kKSteps; ++v) put_a(0, x, (uint32_t)a0[x][v], s2, v);
-                    *reinterpret_cast<i4_t*>(lds + araw[x]) = a1[x];
-                }
-#pragma unroll
-            for (int f = 0; f < kColFrags; ++f) scl[f] = scales2(b_scale_bytes(f, 0));
-            bcur = dequant8((uint32_t)bq[0][0][0], scl[0][0]);
+        for (int x = 0; x < kU; ++x) {
+            const int a = wave + kWaves * x;
+            offSAs[x] = sf_off(m0 + 16 * (a % NA) + ((slane >> 1) & 15));
         }
+        // Offset of the block starting at stage b of the chain: 8 scale
+        // bytes per stage, in row-major scales one atom (512 bytes) per 4
+        // scale columns in blocked ones.
+        auto sblock = [&](int b) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (blocked ? 1024 : kStageK / 16));
+        };
+        auto sload = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+            if (!blocked) return load16(r, voff, soff);
+            i4_t v;
 #pragma unroll
-        for (int i = 0; i < F; ++i)
+            for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b32(r, voff + 512u * j, soff, 0);
+            return v;
+        };
+        // The block offset goes into the per-lane offset, which the buffer's
+        // range check covers (the scalar offset is not checked): a block
+        // that runs past the end of the last row reads zeros there.
+        i4_t sregB, sregA[2];
+        auto scale_load = [&](int b) {
+            sregB = sload(rSB, offSBs + sblock(b), 0);
 #pragma unroll
-            for (int f = 0; f < kColFrags; ++f) acc[i][f] = zero_acc();
-        pin_acc<F>(acc);
-        lds_barrier();
+            for (int x = 0; x < kU; ++x) sregA[x] = sload(rSA, offSAs[x] + sblock(b), 0);
+        };
+        auto scale_store = [&](int buf) {
+            *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][slane >> 1][4 * (slane & 1)]) = sregB;
+#pragma unroll
+            for (int x = 0; x < kU; ++x)
+                *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][32 + 16 * x + ((slane >> 1) & 15)][4 * (slane & 1)]) =
+                    sregA[x];
+        };
+        // The scale dword of this lane for stage t of the chain: B fragment f,
+        // or A unit x.
+        auto scale_b = [&](int t, int f) {
+            return sm.sscr[(t >> 2) & 1][wave][16 * f + c16][2 * (t & 3) + (kq >> 1)];
+        };
+        auto scale_a = [&](int t, int x) {
+            return sm.sscr[(t >> 2) & 1][wave][32 + 16 * x + c16][2 * (t & 3) + (kq >> 1)];
+        };
 
-        // Stage t at ring slot p = t % 2 (the loop below is unrolled by 2,
-        // so p is a compile-time constant and the stage has no branch on it).
-        // The B operands are dequantised one MFMA group ahead: (fragment f,
-        // k-step v) during the MFMAs of the operand before it, (0, 0) of the
-        // next stage during those of (3, 3).
-        auto stage = [&](auto parity, int t) {
-            constexpr int p = decltype(parity)::value;
-            const uint8_t* ard = lds + (uint32_t)p * kABufBytes + (uint32_t)(kh * kKSteps) * kPieceBytes + 16u * lane;
-            auto read_av = [&](int a, int v) {
-                return *reinterpret_cast<const h8_t*>(ard + (uint32_t)a * kAFragBytes + (uint32_t)v * kPieceBytes);
-            };
-            auto read_raw = [&](int x, int v) { return *reinterpret_cast<const uint32_t*>(lds + araw[x] + 4u * v); };
-            uint32_t snext[kColFrags];   // B scale bytes of stage t + 1
-            h2_t as2[kP];                // A scales of stage t + 1
-            uint32_t ar[kP];             // raw A of stage t + 1, dword of the current k-step
-            i4_t anext[kP];              // raw A of stage t + 2
-            h8_t av[F];                  // A operands of the current k-step
-            // Stage start: the A operands of k-step 0, the production's first
-            // raw dword and scales, the raw A of stage t + 2.
+        // Prologue: raw A of stage 0, then ring slot j < kRing (B of stage j,
+        // raw A of stage j + 1), in the order the stages issue their loads;
+        // stage 0 of A into LDS buffer 0.
+        {
+            i4_t a0[2];
+            scale_load(0);
 #pragma unroll
-            for (int a = 0; a < F; ++a) av[a] = read_av(a, 0);
+            for (int x = 0; x < kU; ++x) a0[x] = load16(rA, offA[x], sbyte(0));
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) {
-                    ar[x] = read_raw(x, 0);
-                    as2[x] = a_scales(x, t + 1);
-                    anext[x] = load16(rA, offA[x], soff(t + 2, wave & 1));
-                }
+            for (int j = 0; j < kRing; ++j) {
 #pragma unroll
-            for (int v = 0; v < kKSteps; ++v) {
-                if (v == 2) {
+                for (int f = 0; f < 2; ++f) bq[j][f] = load16(rB, offB[f], sbyte(j));
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int f = 0; f < kColFrags; ++f) snext[f] = b_scale_bytes(f, t + 1);
-                }
-                // The MFMAs of k-step v, fragment-major; the B operand of the
-                // next group is dequantised during each group, and during
-                // the last group the A operands of k-step v + 1 are read into
-                // the registers each MFMA has just consumed.
-                if (v > 0) {
-#pragma unroll
-                    for (int a = 0; a < F; ++a) av[a] = read_av(a, v);
-                }
-#pragma unroll
-                for (int f = 0; f < kColFrags; ++f) {
-#pragma unroll
-                    for (int a = 0; a < F; ++a) {
-                        acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bcur, av[a], acc[a][f], 0, 0, 0);
-                    }
-                    h8_t bnext;
-                    if (f + 1 < kColFrags) {
-                        bnext = dequant8((uint32_t)bq[p][f + 1][v], scl[f + 1][v >> 1]);
-                    } else if (v + 1 < kKSteps) {
-                        bnext = dequant8((uint32_t)bq[p][0][v + 1], scl[0][(v + 1) >> 1]);
-                    } else {
-#pragma unroll
-                        for (int g = 0; g < kColFrags; ++g) scl[g] = scales2(snext[g]);
-                        bnext = dequant8((uint32_t)bq[p ^ 1][0][0], scl[0][0]);
-                    }
-                    // A register of the ring whose last dword was just
-                    // dequantised is re-loaded with stage t + 2.
-                    const int done = f + 1 < kColFrags ? (v == kKSteps - 1 ? f + 1 : -1)
-                                                       : (v == kKSteps - 2 ? 0 : -1);
-                    if (done >= 0) {
-                        fence_after(bnext);
-                        bq[p][done] = load16(rB, offB[done], soff(t + 2, kh));
-                    }
-                    bcur = bnext;
-                }
-                // Dword v of the A pieces of stage t + 1 into the other
-                // buffer (its readers of stage t - 1 passed the last barrier);
-                // the next dword is read one k-step ahead.
-#pragma unroll
-                for (int x = 0; x < kP; ++x)
-                    if (areal[x]) {
-                        put_a(p ^ 1, x, ar[x], as2[x], v);
-                        if (v + 1 < kKSteps)
-                            ar[x] = read_raw(x, v + 1);
-                        else
-                            *reinterpret_cast<i4_t*>(lds + araw[x]) = anext[x];
-                    }
-                if (v == 1) {
-                    if constexpr (p == 0)
-                        stage_store((t >> 1) + 1);
-                    else
-                        stage_load((t >> 1) + 2);
-                }
+                for (int x = 0; x < kU; ++x) aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
-            pin_acc<F>(acc);
+            scale_store(0);
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                const h2_t sa = scales2(scale_a(0, x), sshift);
+#pragma unroll
+                for (int v = 0; v < kKSteps; ++v) adst[x][v * kWave] = dequant8((uint32_t)a0[x][v], sa[v >> 1]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int f = 0; f < 2; ++f) acc[i][f] = zero_acc();
+        lds_barrier();
+
+        // Stage i of the chain, at ring slot p = i % kRing and scale-block
+        // phase q = i % 4, both known at compile time (the loop below is
+        // unrolled by 4), so the stage has no branch: a branch here would
+        // make the compiler's wait counts at its join conservative, which
+        // drains the load ring.
+        auto stage = [&](auto parity, auto phase, int i) {
+            constexpr int p = decltype(parity)::value;
+            constexpr int q = decltype(phase)::value;
+            const uint32_t sb2 = sbyte(i + kRing);
+            const uint32_t sb3 = sbyte(i + 1 + kRing);
+            // LDS A buffers: this stage reads buffer i % 2 and writes the other.
+            const int lb = i & 1;
+            const AStage& ard = sm.a[lb];
+            h8_t* awr[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x)
+                awr[x] = reinterpret_cast<h8_t*>(reinterpret_cast<char*>(adst[x]) + (lb ^ 1) * abuf_step[x]);
+            // Scales of this stage (B) and of the A being dequantised
+            // (stage i + 1, or this one past the chain's end), from the
+            // staging array.  Block b + 1's scales go out at the first stage
+            // of block b and are staged at its third stage, before the A of
+            // its first stage needs them.
+            const int ia = i + 1 < n ? i + 1 : i;
+            const h2_t sbf[2] = {scales2(scale_b(i, 0), sshift), scales2(scale_b(i, 1), sshift)};
+            h2_t saf[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x) saf[x] = scales2(scale_a(ia, x), sshift);
+            // Past the chain's end these read bytes never used (zeros past
+            // the buffer) and fill a staging buffer nobody reads.
+            if constexpr (q == 0) scale_load(i + 4);
+            if constexpr (q == 2) scale_store(((i >> 2) + 1) & 1);
+
+            // k-step pipeline: the B dequant of k-step v + 1 is issued before
+            // the MFMAs of k-step v; the scheduling barrier at the end of each
+            // k-step keeps the compiler from hoisting work across k-steps.
+            h8_t bv[2] = {dequant8((uint32_t)bq[p][0][0], sbf[0][0]), dequant8((uint32_t)bq[p][1][0], sbf[1][0])};
+#pragma unroll
+            for (int v = 0; v < kKSteps; ++v) {
+                h8_t av[NA];
+#pragma unroll
+                for (int a = 0; a < NA; ++a) av[a] = ard.v[a][v][lane];
+                h8_t nbv[2] = {bv[0], bv[1]};
+                if (v + 1 < kKSteps) {
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        nbv[f] = dequant8((uint32_t)bq[p][f][v + 1], sbf[f][(v + 1) >> 1]);
+                }
+#pragma unroll
+                for (int a = 0; a < NA; ++a)
+#pragma unroll
+                    for (int f = 0; f < 2; ++f)
+                        acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bv[f], av[a], acc[a][f], 0, 0, 0);
+                // Piece v of each A unit of stage i + 1 -> the other LDS buffer.
+#pragma unroll
+                for (int x = 0; x < kU; ++x)
+                    awr[x][v * kWave] = dequant8((uint32_t)aq[p][x][v], saf[x][v >> 1]);
+                if (v == kKSteps - 2) {
+                    // B is fully dequantised (the last k-step is in nbv).
+                    fence_after(nbv[0]);
+                    fence_after(nbv[1]);
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) bq[p][f] = load16(rB, offB[f], sb2);
+                }
+                if (v == kKSteps - 1) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int x = 0; x < kU; ++x) aq[p][x] = load16(rA, offA[x], sb3);
+                }
+                bv[0] = nbv[0];
+                bv[1] = nbv[1];
+#if NVFP4_INTERLEAVE
+                // Issue order: the A operands are read from LDS a few MFMAs
+                // ahead of their use (so few are live at once), and the MFMAs
+                // alternate with the VALU work, so the dequantisation runs
+                // while the matrix core is busy.
+                constexpr int kLead = NA <= 8 ? NA : 8;   // A operands read ahead of their MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);   // LDS reads
+#pragma unroll
+                for (int g = 0; g < 2 * NA; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // up to two VALU
+                    if ((g & 1) && (g >> 1) + kLead < NA) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+#endif
+                __builtin_amdgcn_sched_barrier(0);
+            }
             lds_barrier();
         };
 
-        int t = 0;
-        for (; t + 1 < n; t += 2) pair_pass<0, 2>(stage, t);
-        if (t < n) stage(Parity<0>{}, t);
+        int i = 0;
+        for (; i + 3 < n; i += 4) phase_pass<0, 4, kRing>(stage, i);
+        phase_tail<0, 4, kRing>(stage, i, n);
     }
-    finish_segment<F, KH>(args, pos, first_chain, last_chain, lds, s_flag, acc, m0, n0, cg, lane);
+    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
 // ------------------------------------------------------------------ MXFP4
@@ -858,11 +880,11 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 // N x K/32 bytes.  gfx950's block-scaled MFMA takes this form as it is:
 // v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands (format code 4)
 // multiplies each lane's 32 codes by that lane's E8M0 scale.  Lane (c16, kq)
-// supplies row c16 of an operand fragment and 32 K, here the 16 bytes
-// [64 kh + 16 kq, +16) of the row's stage bytes (K half kh of the stage, in
-// the natural nibble order), whose scale is byte 4 kh + kq of the row's 8
-// stage scale bytes.  No dequantisation: one MFMA per fragment pair per K
-// half of a stage.
+// supplies row c16 of an operand fragment and K = 32 kq .. 32 kq + 31 of the
+// 128-K step, which are bytes 16 kq .. 16 kq + 15 of the row's 64 bytes of
+// the stage, in the natural nibble order; its scale is byte 4 s + kq of the
+// row's scales at stage s.  No dequantisation, one MFMA per fragment pair
+// per stage.
 using v8i_t = int __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f4_t mfma_mx(i4_t b, uint32_t sb, i4_t a, uint32_t sa, f4_t c)
@@ -874,178 +896,208 @@ __device__ __forceinline__ f4_t mfma_mx(i4_t b, uint32_t sb, i4_t a, uint32_t sa
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, 4, 4, 0, (int)sb, 0, (int)sa);
 }
 
-// One chain of an MXFP4 tile (same tile shape, stages, K halves, schedule
-// and end of segment as run_segment):
-//   * B: each lane loads its 16 bytes per fragment and stage (the MFMA
-//     operand as it is), two stages ahead in a register ring.
-//   * A: the waves copy the 2 F pieces of the next stage (fragment, K half)
-//     to LDS as they are, piece p by wave p % 8.
-//   * Scales: staged through LDS in blocks of two stages (8 bytes per row
-//     and stage), as in run_segment; each consumer reads its bytes there.
-//     A tile that ends with a 128-K stage gets zero scales and zero A codes
-//     for the missing half of that stage.
-//   * Per stage each wave runs 4 F MFMAs of 16 x 16 x 128; one LDS-only
-//     barrier ends the stage.
-template <int F, int KH>
-__device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
-                                               bool first_chain, bool last_chain, uint8_t* lds, int* s_flag)
+__device__ __forceinline__ uint32_t load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
 {
-    constexpr int kh = KH;
-    constexpr int kP = F > 4 ? 2 : 1;
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// Stages J .. R-1 of a ring pass: f(Parity<J>, i + J) for those below n.
+template <int J, int R, class F>
+__device__ __forceinline__ void ring_tail(F& f, int i, int n)
+{
+    if constexpr (J < R) {
+        if (i + J < n) {
+            f(Parity<J>{}, i + J);
+            ring_tail<J + 1, R>(f, i, n);
+        }
+    }
+}
+
+template <int J, int R, class F>
+__device__ __forceinline__ void ring_pass(F& f, int i)
+{
+    if constexpr (J < R) {
+        f(Parity<J>{}, i + J);
+        ring_pass<J + 1, R>(f, i);
+    }
+}
+
+// One segment of an MXFP4 tile (same tile shape, schedule, wave layout and
+// end of segment as run_segment):
+//   * B: each lane loads 16 bytes of its row per stage (the MFMA operand as
+//     it is) and its scale byte, kRing stages ahead in a register ring.
+//   * A: wave w loads fragment w (and w + 8 for more than 8 fragments) the
+//     same way, one stage ahead of its use, and stores it with its scale
+//     bytes into a double-buffered LDS stage that every wave reads.
+//   * Per stage each wave runs 2 x NA MFMAs of 16 x 16 x 128; one LDS-only
+//     barrier ends the stage.
+template <int MF>
+__device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
+                                               bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
+{
+    constexpr int NA = 2 * MF;
+    constexpr int kU = NA > kWaves ? 2 : 1;
+    // Stages of B in flight.  Measured on MI355X: 2 beats 4 and 4 beats 8
+    // on every workload (a deeper ring's first burst of loads delays every
+    // workgroup's first stage by several us, and one stage ahead already
+    // covers the load latency: a ring of 1 times the same as 2); depths of 6
+    // and 3 compiled to loops whose wait counts drained the ring every pass.
+    constexpr int kRing = 2;
+    // A fragments read from LDS per group (the scheduling barrier between
+    // groups keeps the compiler from loading every fragment of the stage up
+    // front, which large tiles have no registers for).
+    constexpr int kAGroup = MF <= 4 ? NA : 4;
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int cg = wave & 3;
     const int lane = tid % kWave;
-    const int c16 = lane & 15, kq = lane >> 4;
+    const int c16 = lane & 15;
+    const int kq = lane >> 4;
     const int M = ga.M, N = ga.N, K = ga.K;
     const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 32;
-    const int last_stage = gs.stages - 1;
-    const bool half_last = (K % kStageK) != 0;
 
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(ga.A, (uint32_t)M * row_bytes);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(ga.B, (uint32_t)N * row_bytes);
     const __amdgpu_buffer_rsrc_t rSA = make_rsrc(ga.SFA, (uint32_t)M * row_scales);
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
 
-    uint32_t offB[kColFrags];
+    // Rows past M or N are beyond the buffers and read zeros.
+    uint32_t offB[2], offSB[2];
 #pragma unroll
-    for (int f = 0; f < kColFrags; ++f)
-        offB[f] = (uint32_t)(n0 + 64 * cg + 16 * f + c16) * row_bytes + 64u * kh + 16u * kq;
-    const uint32_t sbsrc = kMxScaleOff + (uint32_t)(64 * cg + c16) * kMxSRow + 4u * kh + (uint32_t)kq;
-    const uint32_t sasrc = kMxScaleOff + kMxSBBytes + (uint32_t)c16 * kMxSRow + 4u * kh + (uint32_t)kq;
-
-    bool areal[kP];
-    bool ahalf1[kP];
-    uint32_t offA[kP], adst[kP];
+    for (int f = 0; f < 2; ++f) {
+        const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
+        offB[f] = brow * row_bytes + 16u * kq;
+        offSB[f] = brow * row_scales + (uint32_t)kq;
+    }
+    uint32_t offA[2], offSA[2];
 #pragma unroll
-    for (int x = 0; x < kP; ++x) {
-        const int p = wave + 8 * x;
-        areal[x] = (x == 0 && F >= 4) || p < 2 * F;   // waves are 0..7
-        const int a = areal[x] ? p >> 1 : 0, h = p & 1;
-        ahalf1[x] = h == 1;
-        offA[x] = (uint32_t)(m0 + 16 * a + c16) * row_bytes + 64u * h + 16u * kq;
-        adst[x] = (uint32_t)(a * 2 + h) * kPieceBytes + 16u * lane;
+    for (int x = 0; x < kU; ++x) {
+        const int a = wave + kWaves * x;
+        const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);
+        offA[x] = arow * row_bytes + 16u * kq;
+        offSA[x] = arow * row_scales + (uint32_t)kq;
     }
 
-    f4_t acc[F][kColFrags];
+    f4_t acc[NA][2];
 #pragma unroll
-    for (int i = 0; i < F; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-        for (int f = 0; f < kColFrags; ++f) acc[i][f] = zero_acc();
+        for (int f = 0; f < 2; ++f) acc[i][f] = zero_acc();
 
     {
         const int n = s_end - s_begin;
-        auto sidx = [&](int j) { return s_begin + (j < n ? j : n - 1); };
-        // As in run_segment: K half 1 of a 128-K last stage re-reads bytes
-        // of its row (its A codes are zeroed, its scales are zero).
-        const int half1_max = (int)row_bytes - kStageBytes > 0 ? (int)row_bytes - kStageBytes : 0;
-        auto soff = [&](int j, int h) {
-            const int o = sidx(j) * kStageBytes;
-            return (uint32_t)__builtin_amdgcn_readfirstlane(h == 1 && o > half1_max ? half1_max : o);
+        // Stage offsets in a row of codes and of scales; stages past the
+        // chain repeat its last stage (loaded, never used).
+        auto sbyte = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
         };
-        auto sblk = [&](int j) { return (uint32_t)((j >> 1) & 1) * kMxSBlockBytes + 8u * (uint32_t)(j & 1); };
-        auto lds_u8 = [&](uint32_t off) -> uint32_t { return lds[off]; };
-
-        // Scale staging: thread t loads the 8 scale bytes of stage t % 2 of
-        // B row t / 2 (and waves 0-2 of A row t / 2), as two 4-byte loads,
-        // so that the second half of a 128-K last stage (past the row's
-        // scales) is read by none.
-        uint2 stb, sta;
-        auto stage_load = [&](int beta) {
-            const int part = tid & 1, r = tid >> 1;
-            const int sg = sidx(2 * beta + part);
-            const bool hs = half_last && sg == last_stage;
-            auto load_row = [&](__amdgpu_buffer_rsrc_t rs, int row) {
-                const uint32_t o = (uint32_t)row * row_scales + 8u * (uint32_t)sg;
-                return uint2{__builtin_amdgcn_raw_buffer_load_b32(rs, o, 0, 0),
-                             __builtin_amdgcn_raw_buffer_load_b32(rs, hs ? kNoLoad : o + 4u, 0, 0)};
-            };
-            stb = load_row(rSB, n0 + r);
-            if (wave < 3) sta = load_row(rSA, m0 + r);
+        auto sscl = [&](int t) {
+            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 32));
         };
-        auto stage_store = [&](int beta, uint2 vb, uint2 va) {
-            uint8_t* blk = lds + kMxScaleOff + (uint32_t)(beta & 1) * kMxSBlockBytes;
-            *reinterpret_cast<uint2*>(blk + 8u * tid) = vb;
-            if (wave < 3) *reinterpret_cast<uint2*>(blk + kMxSBBytes + 8u * tid) = va;
+        // A stores of waves whose unit is past the tile's fragments go to a
+        // discard area, so the stage has no branch (a branch would let the
+        // compiler sink each stage's MFMAs into later blocks).
+        i4_t* vdst[2];
+        uint32_t* sdst[2];
+        uint32_t mstep[2];
+#pragma unroll
+        for (int x = 0; x < kU; ++x) {
+            const int a = wave + kWaves * x;
+            const bool real = a < NA;
+            vdst[x] = real ? &sm.mx[0].v[a][lane] : reinterpret_cast<i4_t*>(&sm.discard[0][0]) + lane;
+            sdst[x] = real ? &sm.mx[0].s[a][lane]
+                           : reinterpret_cast<uint32_t*>(reinterpret_cast<i4_t*>(&sm.discard[0][0]) + kWave) + lane;
+            mstep[x] = real ? (uint32_t)sizeof(MxStage) : 0u;
+        }
+        auto put_a = [&](int buf, int x, i4_t v, uint32_t sc) {
+            *reinterpret_cast<i4_t*>(reinterpret_cast<char*>(vdst[x]) + buf * mstep[x]) = v;
+            *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sdst[x]) + buf * mstep[x]) = sc;
         };
 
-        i4_t bq[2][kColFrags], aq[2][kP];
-        auto load_b = [&](int slot, int j) {
-#pragma unroll
-            for (int f = 0; f < kColFrags; ++f) bq[slot][f] = load16(rB, offB[f], soff(j, kh));
-        };
-        auto load_a = [&](int slot, int j) {
-#pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) aq[slot][x] = load16(rA, offA[x], soff(j, wave & 1));
-        };
-        // Raw A of chain stage j into buffer buf (zero codes for the missing
-        // half of a 128-K last stage).
-        auto put_a = [&](int buf, int x, i4_t q, int j) {
-            if (ahalf1[x] && half_last && sidx(j) == last_stage) q = i4_t{0, 0, 0, 0};
-            *reinterpret_cast<i4_t*>(lds + kMxABufBytes * (uint32_t)buf + adst[x]) = q;
-        };
+        i4_t bq[kRing][2], aq[kRing][2];
+        uint32_t bs[kRing][2], as[kRing][2];
         {
-            // Scale block 0 and the raw A of stage 0 first, then the loads
-            // in the order two stages of the loop issue them (so the waits
-            // the compiler derives for the loop's first stage are those of
-            // every other).
-            i4_t a0[kP];
-            stage_load(0);
-            const uint2 st0b = stb, st0a = sta;
+            i4_t a0[2];
+            uint32_t s0[2];
 #pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) a0[x] = load16(rA, offA[x], soff(0, wave & 1));
-            load_b(0, 0);
-            load_a(1, 1);
-            stage_load(1);
-            load_b(1, 1);
-            load_a(0, 2);
-            stage_store(0, st0b, st0a);
+            for (int x = 0; x < kU; ++x) {
+                a0[x] = load16(rA, offA[x], sbyte(0));
+                s0[x] = load_u8(rSA, offSA[x], sscl(0));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) put_a(0, x, a0[x], 0);
+            for (int j = 0; j < kRing; ++j) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                    bq[j][f] = load16(rB, offB[f], sbyte(j));
+                    bs[j][f] = load_u8(rSB, offSB[f], sscl(j));
+                }
+#pragma unroll
+                for (int x = 0; x < kU; ++x) {
+                    aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
+                    as[j][x] = load_u8(rSA, offSA[x], sscl(j + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int x = 0; x < kU; ++x) put_a(0, x, a0[x], s0[x]);
         }
         lds_barrier();
 
-        auto stage = [&](auto parity, int t) {
+        auto stage = [&](auto parity, int i) {
             constexpr int p = decltype(parity)::value;
-            uint32_t sb[kColFrags];
+            const int lb = i & 1;
 #pragma unroll
-            for (int f = 0; f < kColFrags; ++f) sb[f] = lds_u8(sbsrc + sblk(t) + 16u * kMxSRow * f);
+            for (int a0 = 0; a0 < NA; a0 += kAGroup) {
 #pragma unroll
-            for (int a = 0; a < F; ++a) {
-                const i4_t av = *reinterpret_cast<const i4_t*>(lds + kMxABufBytes * (uint32_t)p +
-                                                               (uint32_t)(a * 2 + kh) * kPieceBytes + 16u * lane);
-                const uint32_t sa = lds_u8(sasrc + sblk(t) + 16u * kMxSRow * a);
+                for (int a = a0; a < a0 + kAGroup && a < NA; ++a) {
+                    const i4_t av = sm.mx[lb].v[a][lane];
+                    const uint32_t sa = sm.mx[lb].s[a][lane];
 #pragma unroll
-                for (int f = 0; f < kColFrags; ++f) acc[a][f] = mfma_mx(bq[p][f], sb[f], av, sa, acc[a][f]);
+                    for (int f = 0; f < 2; ++f) acc[a][f] = mfma_mx(bq[p][f], bs[p][f], av, sa, acc[a][f]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // A of stage t + 1 into the other buffer (its readers of stage
-            // t - 1 passed the previous barrier), then the ring slots'
-            // re-loads: B of stage t + 2, A of stage t + 3.
+            // A of stage i + 1 into the other buffer (its readers of stage
+            // i - 1 passed the previous barrier), then the ring slot's
+            // reloads: B of stage i + kRing, A of stage i + 1 + kRing.
 #pragma unroll
-            for (int x = 0; x < kP; ++x)
-                if (areal[x]) put_a(p ^ 1, x, aq[p ^ 1][x], t + 1);
-            load_b(p, t + 2);
-            load_a(p ^ 1, t + 3);
-            if constexpr (p == 0)
-                stage_store((t >> 1) + 1, stb, sta);
-            else
-                stage_load((t >> 1) + 2);
-            pin_acc<F>(acc);
+            for (int x = 0; x < kU; ++x) put_a(lb ^ 1, x, aq[p][x], as[p][x]);
+            // The slot's old values are consumed before its reloads are
+            // issued, so the reloads can take the same registers (otherwise
+            // the compiler copies ring values whose loads are in flight and
+            // waits for them).
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                fence_after(bq[p][f]);
+                fence_after(bs[p][f]);
+            }
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                fence_after(aq[p][x]);
+                fence_after(as[p][x]);
+            }
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                bq[p][f] = load16(rB, offB[f], sbyte(i + kRing));
+                bs[p][f] = load_u8(rSB, offSB[f], sscl(i + kRing));
+            }
+#pragma unroll
+            for (int x = 0; x < kU; ++x) {
+                aq[p][x] = load16(rA, offA[x], sbyte(i + 1 + kRing));
+                as[p][x] = load_u8(rSA, offSA[x], sscl(i + 1 + kRing));
+            }
             lds_barrier();
         };
-        int t = 0;
-        for (; t + 1 < n; t += 2) pair_pass<0, 2>(stage, t);
-        if (t < n) stage(Parity<0>{}, t);
+        int i = 0;
+        for (; i + kRing - 1 < n; i += kRing) ring_pass<0, kRing>(stage, i);
+        ring_tail<0, kRing>(stage, i, n);
     }
-    finish_segment<F, KH>(args, pos, first_chain, last_chain, lds, s_flag, acc, m0, n0, cg, lane);
+    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
 // Wave-uniform values computed in vector registers (64-bit divisions have
@@ -1072,31 +1124,11 @@ __device__ __forceinline__ Pos uniform(const Pos& p)
     return r;
 }
 
-// One chain, each wave running the code of its K half (waves 0-3 half 0,
-// waves 4-7 half 1).  Both halves meet the same barriers in the same order.
-template <bool kMx, bool kBlocked, int F>
-__device__ __forceinline__ void run_chain(const LaunchArgs& args, const Pos& pos, int c0, int c1, bool first,
-                                          bool last, uint8_t* lds, int* s_flag)
-{
-    const bool half1 = __builtin_amdgcn_readfirstlane(opaque_tid() / kWave) >= kColGroups;
-    if constexpr (kMx) {
-        if (half1)
-            run_segment_mx<F, 1>(args, pos, c0, c1, first, last, lds, s_flag);
-        else
-            run_segment_mx<F, 0>(args, pos, c0, c1, first, last, lds, s_flag);
-    } else {
-        if (half1)
-            run_segment<F, kBlocked, 1>(args, pos, c0, c1, first, last, lds, s_flag);
-        else
-            run_segment<F, kBlocked, 0>(args, pos, c0, c1, first, last, lds, s_flag);
-    }
-}
-
 // The persistent walk of one workgroup over its cost range: every segment
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
 template <bool kMx, bool kBlocked>
-__device__ __forceinline__ void walk_range(const LaunchArgs& args, uint8_t* lds, int* s_flag)
+__device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
     const int w = uniform(worker_id(args.G));
     const int64_t b1 = uniform(boundary(args.W, args.G, w + 1));
@@ -1111,13 +1143,24 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, uint8_t* lds,
         for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
             const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
             const bool first = c0 == pos.stage, last = c1 == s_end;
-            switch (pos.frags) {
-                case 1: run_chain<kMx, kBlocked, 1>(args, pos, c0, c1, first, last, lds, s_flag); break;
-                case 2: run_chain<kMx, kBlocked, 2>(args, pos, c0, c1, first, last, lds, s_flag); break;
-                case 3: run_chain<kMx, kBlocked, 3>(args, pos, c0, c1, first, last, lds, s_flag); break;
-                case 4: run_chain<kMx, kBlocked, 4>(args, pos, c0, c1, first, last, lds, s_flag); break;
-                case 5: run_chain<kMx, kBlocked, 5>(args, pos, c0, c1, first, last, lds, s_flag); break;
-                default: run_chain<kMx, kBlocked, 6>(args, pos, c0, c1, first, last, lds, s_flag); break;
+            if constexpr (kMx) {
+                switch (pos.frags) {
+                    case 1: run_segment_mx<1>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 2: run_segment_mx<2>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 3: run_segment_mx<3>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 4: run_segment_mx<4>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 5: run_segment_mx<5>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    default: run_segment_mx<6>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                }
+            } else {
+                switch (pos.frags) {
+                    case 1: run_segment<1, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 2: run_segment<2, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 3: run_segment<3, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 4: run_segment<4, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    case 5: run_segment<5, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                    default: run_segment<6, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
+                }
             }
         }
         if (s_end < gs.stages) break;
@@ -1127,24 +1170,24 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, uint8_t* lds,
 
 __global__ __launch_bounds__(kThreads) void nvfp4_group_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ SharedMem sm;
     __shared__ int s_flag;
-    walk_range<false, false>(args, lds, &s_flag);
+    walk_range<false, false>(args, sm, &s_flag);
 }
 
 // NVFP4 with the scales in the blocked layout.
 __global__ __launch_bounds__(kThreads) void nvfp4_blocked_sf_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ SharedMem sm;
     __shared__ int s_flag;
-    walk_range<false, true>(args, lds, &s_flag);
+    walk_range<false, true>(args, sm, &s_flag);
 }
 
 __global__ __launch_bounds__(kThreads) void mxfp4_group_gemm_kernel(const LaunchArgs args)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ SharedMem sm;
     __shared__ int s_flag;
-    walk_range<true, false>(args, lds, &s_flag);
+    walk_range<true, false>(args, sm, &s_flag);
 }
 
 // Writes zeros to C of a group with K == 0 (the empty sum).
@@ -1195,6 +1238,7 @@ int fail(int code, const std::string& msg)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+
 // Workspace of the split-tile fix-up, one per (device, stream): kSlotsPerWG
 // partial-tile slots per workgroup and one counter per workgroup (zero
 // between calls; the workgroup that finishes a tile resets its counter).
@@ -1202,7 +1246,7 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // allocated by the first call on the pair and never resized or freed, so a
 // later call on it allocates, frees and synchronises nothing.
 struct Workspace {
-    uint8_t* partials = nullptr;
+    float* partials = nullptr;
     int* counters = nullptr;
     int workers = 0;
 };
@@ -1231,7 +1275,9 @@ int get_workspace(int dev, hipStream_t s, Workspace& out)
     }
     Workspace w;
     w.workers = device_cus_locked(dev);
-    const size_t pbytes = (size_t)kSlotsPerWG * w.workers * kSlotBytes;
+    if ((uint64_t)kSlotsPerWG * w.workers * kSlotFloats * 4u >= kNoSlot)
+        return fail(NVFP4GG_UNSUPPORTED, "too many compute units for the partial-tile workspace");
+    const size_t pbytes = (size_t)kSlotsPerWG * w.workers * kSlotFloats * sizeof(float);
     if (hipMalloc(&w.partials, pbytes) != hipSuccess) return fail(NVFP4GG_HIP_ERROR, "workspace allocation failed");
     if (hipMalloc(&w.counters, (size_t)w.workers * sizeof(int)) != hipSuccess) {
         (void)hipFree(w.partials);
@@ -1297,7 +1343,7 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         for (const void* p : ops)
             if (!p || !aligned16(p))
                 return fail(NVFP4GG_INVALID_ARG, gs + "an operand pointer is NULL or not 16-byte aligned");
-        if (K[i] % (kStageK / 2) != 0)
+        if (K[i] % kStageK != 0)
             return fail(NVFP4GG_UNSUPPORTED, gs + "this kernel needs K % 128 == 0");
         // Byte offsets of the buffer loads are 32-bit and may run one tile
         // past the last row.
@@ -1372,10 +1418,9 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
             tiles += sc.mblocks * sc.nblocks;
         }
         args.ngroups = n;
+        args.blocked_sf = blocked_sf;
         args.W = cost;
         args.G = grid_size(cost, ws.workers);
-        if ((uint64_t)kSlotsPerWG * args.G * kSlotBytes >= ((uint64_t)1 << 32))
-            return fail(NVFP4GG_UNSUPPORTED, "too many compute units for the partial-tile workspace");
         args.partials = ws.partials;
         args.counters = ws.counters;
         const void* kernel = fmt == kFmtMxfp4 ? reinterpret_cast<const void*>(&mxfp4_group_gemm_kernel)

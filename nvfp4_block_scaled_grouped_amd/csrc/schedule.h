@@ -5,10 +5,9 @@
 // launcher include it, and a CPU test compiles it on its own.
 //
 // Terms:
-//   * fragment: 16 rows of A_i (the MFMA tile height), so a group's last
-//     fragment carries at most 15 padding rows.
+//   * fragment: 32 rows of A_i (the MFMA tile height).
 //   * m-block: up to maxf <= kMaxFrags fragments of one group, processed
-//     together (maxf is chosen per launch).  A group with F = ceil(M/16)
+//     together (maxf is chosen per launch).  A group with F = ceil(M/32)
 //     fragments has nmb = ceil(F / maxf) m-blocks; fragments are spread
 //     evenly, so the first F % nmb m-blocks get F / nmb + 1 fragments and
 //     the rest F / nmb.
@@ -16,16 +15,16 @@
 //   * tile: (group, n-block, m-block); tiles are ordered by group, then
 //     n-block, then m-block, so the m-blocks that share a B strip are
 //     adjacent in the order.
-//   * stage: kStageK consecutive K of a tile (a tile whose K is an odd
-//     multiple of 128 ends with a stage of 128 K).  A stage of a tile with
-//     f fragments costs unit_cost(f, fmt) units (about 10 ns of MI355X time
+//   * stage: kStageK consecutive K of a tile.  A stage of a tile with f
+//     fragments costs unit_cost(f, fmt) units (about 50 ns of MI355X time
 //     each, fitted to measured stage times).  NVFP4 (fp16 MFMA after
 //     dequantisation): the B stream and its dequantisation do not grow with
-//     f, the MFMAs do.  MXFP4 (native FP4 MFMA, no dequantisation): a stage
-//     is mostly its B stream.
+//     f, the MFMAs do, and tiles of more than 4 fragments give every wave a
+//     second piece of A to dequantise.  MXFP4 (native FP4 MFMA, no
+//     dequantisation): a stage is mostly its B stream.
 //   * A tile's cost range is kTileCost (the start-up and wind-down of the
-//     segment that starts it: first loads, the exchange of the two K halves,
-//     the output store) followed by its stages.
+//     segment that starts it: first loads, partial-tile stores, the fix-up)
+//     followed by its stages.
 //   * Workgroup w of G takes the cost range [w*W/G, (w+1)*W/G), rounded up
 //     to stage starts, so every stage belongs to exactly one workgroup.
 #ifndef NVFP4GG_SCHEDULE_H
@@ -42,26 +41,26 @@
 namespace nvfp4sched {
 
 constexpr int kMaxFrags = 6;       // fragments per m-block
-constexpr int kFragRows = 16;      // rows per fragment
+constexpr int kFragRows = 32;      // rows per fragment
 constexpr int kTileN = 256;        // columns per n-block
-constexpr int kStageK = 256;       // K per stage
+constexpr int kStageK = 128;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
-constexpr int kTileCost = 250;     // cost units of a tile beyond its stages
-constexpr int kMaxUnitCost = 164;  // the costliest stage (NVFP4, 6 fragments)
+constexpr int kTileCost = 200;     // cost units of a tile beyond its stages
+constexpr int kMaxUnitCost = 56;   // the costliest stage (NVFP4, 6 fragments)
 constexpr int kFmtNvfp4 = 0;       // E4M3 scale per 16 K, fp16 MFMA
 constexpr int kFmtMxfp4 = 1;       // E8M0 scale per 32 K, FP4 MFMA
 // Least cost handed to one workgroup: keeps every workgroup range longer
 // than the costliest stage, so the workgroups sharing a tile are
 // consecutive.
-constexpr int64_t kMinUnitsPerWG = 256;
+constexpr int64_t kMinUnitsPerWG = 64;
 static_assert(kMinUnitsPerWG >= kMaxUnitCost, "a workgroup range must hold a stage");
 
 struct GroupSched {
     int64_t cost_begin;   // cost units before this group
-    int frags;            // ceil(M / kFragRows)
-    int mblocks;          // ceil(frags / maxf)
+    int frags;            // ceil(M / 32)
+    int mblocks;          // ceil(frags / kMaxFrags)
     int nblocks;          // ceil(N / kTileN)
-    int stages;           // ceil(K / kStageK)
+    int stages;           // K / kStageK
     int tile_begin;       // tiles before this group
     int fmt;              // kFmtNvfp4 or kFmtMxfp4 (selects the stage costs)
 };
@@ -69,7 +68,7 @@ struct GroupSched {
 NVFP4_HD int ceil_div_i(int a, int b) { return (a + b - 1) / b; }
 
 // The schedule entry of a group with M, N >= 1 and K a positive multiple of
-// 128, in m-blocks of at most maxf (1..kMaxFrags) fragments.
+// kStageK, in m-blocks of at most maxf (1..kMaxFrags) fragments.
 NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, int tile_begin, int maxf = kMaxFrags,
                                      int fmt = kFmtNvfp4)
 {
@@ -80,17 +79,18 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
     g.frags = ceil_div_i(M, kFragRows);
     g.mblocks = ceil_div_i(g.frags, maxf);
     g.nblocks = ceil_div_i(N, kTileN);
-    g.stages = ceil_div_i(K, kStageK);
+    g.stages = K / kStageK;
     return g;
 }
 
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
-// about 10 ns.  NVFP4: the MFMAs grow with f, the B stream and its
-// dequantisation do not.  MXFP4: mostly the B stream.
+// about 50 ns.  NVFP4: measured MI355X stage times 1.2, 1.45, 1.75, 2.3 and
+// 2.8 us for 2 to 6 fragments, one fragment extrapolated.  MXFP4: measured
+// 1.15, 1.25, 1.3 and 1.8 us for 2, 3, 4 and 5-6 fragments.
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    if (fmt == kFmtMxfp4) return 80 + 4 * f;
-    return 20 + 24 * f;
+    if (fmt == kFmtMxfp4) return f <= 1 ? 22 : f == 2 ? 23 : f == 3 ? 25 : f == 4 ? 26 : 36;
+    return f <= 1 ? 21 : f == 2 ? 24 : f == 3 ? 29 : f == 4 ? 35 : f == 5 ? 46 : kMaxUnitCost;
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
@@ -186,9 +186,9 @@ NVFP4_HD int grid_size(int64_t W, int cus)
     return (int)G;
 }
 
-// Cost of splitting a tile once more: one more partial tile stored by a
-// contributor and read back by the fix-up.
-constexpr int kSplitCost = 200;
+// Cost of splitting a tile once more (about 3.9 us, measured): one more
+// partial tile stored by a contributor and read back by the fix-up.
+constexpr int kSplitCost = 78;
 
 // Estimated time of a launch of total cost W over G workgroups holding
 // `tiles` tiles, in cost units: one workgroup's range, plus kSplitCost for

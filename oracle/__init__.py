@@ -24,11 +24,11 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP).  Returns the library path."""
+    """Compile the oracle with gcc (-O3, OpenMP).  Returns the library path."""
     if not force and os.path.exists(_LIB_PATH):
         return _LIB_PATH
     tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+    cmd = ["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c11",
            "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB_PATH)

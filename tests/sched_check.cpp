@@ -145,7 +145,7 @@ int main()
         for (int i = 0; i < ng; ++i) {
             M.push_back(1 + rng() % 700);
             N.push_back(1 + rng() % 3000);
-            K.push_back(128 * (1 + rng() % 48));   // odd multiples of 128 end with a 128-K stage
+            K.push_back(kStageK * (1 + rng() % 48));
         }
         const int cus = 1 + rng() % 300;
         const int fmt = (it / 2) % 2 ? kFmtMxfp4 : kFmtNvfp4;

@@ -3,10 +3,9 @@ layout) on the GPU, through the C ABI.
 
 The blocked scale arrays are made from the row-major ones by the oracle's
 layout function (pad bytes 0x7F, an E4M3 NaN, so a kernel that read a pad
-byte into a result would produce NaN there).  Small problems are compared
-element by element with the oracle; the five workloads at full size must give
-bit-for-bit the output of the row-major entry point, which the other parity
-tests check against the oracle.
+byte into a result would produce NaN there).  Problems are compared
+element by element with the oracle (the larger workloads at full size are in
+test_gpu_full.py).
 """
 from __future__ import annotations
 
@@ -69,15 +68,3 @@ def test_blocked_parity(nv, oracle_lib, M, N, K):
     C = _run(nv, M, N, K, A, B, _blocked(oracle_lib, SA, M, K), _blocked(oracle_lib, SB, N, K), True)
     for i in range(len(M)):
         _compare.assert_close(C[i], C_ref[i], X[i], "group %d" % i)
-
-
-@pytest.mark.parametrize("cfg", workloads.CONFIGS, ids=[c["name"] for c in workloads.CONFIGS])
-def test_blocked_workload_equals_row_major(nv, oracle_lib, cfg):
-    M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    _say("blocked workload %s" % cfg["name"])
-    A, B, SA, SB = workloads.config_inputs(cfg)
-    C_rm = _run(nv, M, N, K, A, B, SA, SB, False)
-    C_bl = _run(nv, M, N, K, A, B, _blocked(oracle_lib, SA, M, K), _blocked(oracle_lib, SB, N, K), True)
-    for i in range(len(M)):
-        assert not np.isnan(C_bl[i].astype(np.float32)).any(), "NaN or unwritten output in group %d" % i
-        np.testing.assert_array_equal(C_bl[i].view(np.uint16), C_rm[i].view(np.uint16))
