@@ -79,6 +79,25 @@ int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
                      const void* const* SFA_ptrs, const void* const* SFB_ptrs,
                      void* const* C_ptrs, void* stream);
 
+/* nvfp4_group_gemm for callers that cannot allocate device memory (code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments, kernels, results and return codes,
+ * but the split-tile workspace is a static device array of the library
+ * (144 MiB of partial tiles and 1 KiB of counters, the workspace of 256
+ * workgroups) instead of the per-stream one, so no call allocates, frees or
+ * synchronises.  Each device holds its own copy from the first use of the
+ * library on it until the process ends; the first call on a device looks up
+ * its address (hipGetSymbolAddress).  Every call first clears the counters
+ * with a small kernel on `stream`.  A device with more than 256 compute
+ * units is rejected (NVFP4GG_UNSUPPORTED): its launches could need more
+ * workspace than the array holds.  All calls on one device share the one
+ * array, so calls that overlap on a device (from different streams or
+ * threads) race and give wrong results: the caller serialises them. */
+int nvfp4_group_gemm_noalloc(int g, const int* M, const int* N, const int* K,
+                             const void* const* A_ptrs, const void* const* B_ptrs,
+                             const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                             void* const* C_ptrs, void* stream);
+
 /* The same grouped GEMM with SFA_i and SFB_i in the blocked scale layout
  * that the pages' kernels consume (page 482006: to_blocked_gpu in its cuBLAS
  * path, and the scale-factor layout atom of its CuTe kernel, shape
@@ -162,10 +181,10 @@ int nvfp4_group_gemm_set_max_frags(int frags);
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* nvfp4_group_gemm_last_error(void);
 
-/* ABI version of this header: 6 (2 added nvfp4_group_gemm_blocked, 3
+/* ABI version of this header: 7 (2 added nvfp4_group_gemm_blocked, 3
  * mxfp4_group_gemm, 4 nvfp4_group_gemm_set_wait_limit, 5
  * nvfp4_group_gemm_batched, 6 nvfp4_group_gemm_set_max_frags and the
- * workspace that no longer grows). */
+ * workspace that no longer grows, 7 nvfp4_group_gemm_noalloc). */
 int nvfp4_group_gemm_version(void);
 
 #ifdef __cplusplus

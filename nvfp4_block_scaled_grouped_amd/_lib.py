@@ -33,7 +33,8 @@ def load():
     lib = ctypes.CDLL(LIB_PATH)
     ip = ctypes.POINTER(ctypes.c_int)
     pp = ctypes.POINTER(ctypes.c_void_p)
-    for fn in (lib.nvfp4_group_gemm, lib.nvfp4_group_gemm_blocked, lib.mxfp4_group_gemm):
+    for fn in (lib.nvfp4_group_gemm, lib.nvfp4_group_gemm_blocked, lib.mxfp4_group_gemm,
+               lib.nvfp4_group_gemm_noalloc):
         fn.argtypes = [ctypes.c_int, ip, ip, ip, pp, pp, pp, pp, pp, ctypes.c_void_p]
         fn.restype = ctypes.c_int
     lib.nvfp4_dequant_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -86,7 +87,11 @@ def _ptr(t, name, dtype_names):
 _BYTES = ("uint8", "int8", "float4_e2m1fn_x2", "float8_e4m3fn")
 
 
-def _entry(lib, blocked, fmt):
+def _entry(lib, blocked, fmt, noalloc=False):
+    if noalloc:
+        if blocked or fmt != "nvfp4":
+            raise ValueError("the no-allocation entry point takes NVFP4 row-major scales only")
+        return lib.nvfp4_group_gemm_noalloc
     if fmt == "mxfp4":
         if blocked:
             raise ValueError("the MXFP4 entry point takes row-major scales only")
@@ -96,15 +101,15 @@ def _entry(lib, blocked, fmt):
     return lib.nvfp4_group_gemm_blocked if blocked else lib.nvfp4_group_gemm
 
 
-def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False, fmt="nvfp4") -> int:
+def group_gemm_ptrs(M, N, K, A, B, SFA, SFB, C, stream=0, blocked=False, fmt="nvfp4", noalloc=False) -> int:
     """Raw call: sizes are Python ints, operands are integer device addresses.
     blocked selects nvfp4_group_gemm_blocked (scales in the blocked layout),
-    fmt="mxfp4" mxfp4_group_gemm.  Returns the library's status code without
-    raising."""
+    fmt="mxfp4" mxfp4_group_gemm, noalloc nvfp4_group_gemm_noalloc.  Returns
+    the library's status code without raising."""
     g = len(M)
     lib = load()
     arr = lambda vals, ct: (ct * g)(*vals)
-    fn = _entry(lib, blocked, fmt)
+    fn = _entry(lib, blocked, fmt, noalloc)
     return fn(
         g, arr([int(v) for v in M], ctypes.c_int), arr([int(v) for v in N], ctypes.c_int),
         arr([int(v) for v in K], ctypes.c_int),
@@ -173,7 +178,8 @@ def group_gemm_batched(A, B, SFA, SFB, C, M, N, K, L, stream=None):
     return C
 
 
-def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=False, fmt="nvfp4"):
+def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=False, fmt="nvfp4",
+               noalloc=False):
     """C_i = A_i . B_i^T for every group (see include/nvfp4gg.h).
 
     A, B, SFA, SFB: lists of contiguous uint8 device tensors holding the packed
@@ -183,6 +189,7 @@ def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=F
     C: list of contiguous float16 device tensors (M_i*N_i elements), written.
     M, N, K: sizes; taken from C's and A's shapes when omitted
     (C_i as (M_i, N_i), A_i as (M_i, K_i/2)).
+    noalloc: call nvfp4_group_gemm_noalloc (static workspace, NVFP4 only).
     """
     g = len(A)
     if not (len(B) == len(SFA) == len(SFB) == len(C) == g):
@@ -207,7 +214,8 @@ def group_gemm(A, B, SFA, SFB, C, M=None, N=None, K=None, stream=None, blocked=F
     psa = [_ptr(t, "SFA", _BYTES) for t in SFA]
     psb = [_ptr(t, "SFB", _BYTES) for t in SFB]
     pc = [_ptr(t, "C", ("float16",)) for t in C]
-    _check(group_gemm_ptrs(M, N, K, pa, pb, psa, psb, pc, _stream_handle(stream), blocked=blocked, fmt=fmt))
+    _check(group_gemm_ptrs(M, N, K, pa, pb, psa, psb, pc, _stream_handle(stream), blocked=blocked, fmt=fmt,
+                           noalloc=noalloc))
     return C
 
 

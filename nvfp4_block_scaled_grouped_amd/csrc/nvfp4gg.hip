@@ -1191,6 +1191,27 @@ __global__ __launch_bounds__(kThreads) void mxfp4_group_gemm_kernel(const Launch
 }
 
 // Writes zeros to C of a group with K == 0 (the empty sum).
+// Scratch of nvfp4_group_gemm_noalloc (the workspace of the split-tile
+// fix-up for callers that cannot allocate): the partial-tile slots of
+// kScratchWorkers workgroups, then one counter per workgroup.  Each device
+// the library runs on holds its own copy, from the load of the library's
+// code on it until the process ends.  Host code never uses this name as an
+// address: it takes the device's copy from hipGetSymbolAddress.
+constexpr int kScratchWorkers = 256;
+constexpr size_t kScratchPartialBytes = (size_t)kSlotsPerWG * kScratchWorkers * kSlotFloats * sizeof(float);
+constexpr size_t kScratchBytes = kScratchPartialBytes + (size_t)kScratchWorkers * sizeof(int);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static_assert(kScratchPartialBytes % 256 == 0, "the counters start 256-byte aligned");
+static_assert(kScratchPartialBytes < kNoSlot, "the partial slots stay below the zero-read offset");
+
+// counters[0 .. n) = 0 (before a call that uses the static scratch: that
+// memory keeps whatever the previous call left).
+__global__ __launch_bounds__(256) void clear_counters_kernel(int* counters, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) counters[i] = 0;
+}
+
 __global__ __launch_bounds__(256) void zero_fill_kernel(uint16_t* C, int64_t count)
 {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
@@ -1302,7 +1323,7 @@ std::atomic<int> g_max_frags{0};
 
 extern "C" const char* nvfp4_group_gemm_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int nvfp4_group_gemm_version(void) { return 6; }
+extern "C" int nvfp4_group_gemm_version(void) { return 7; }
 
 extern "C" int nvfp4_group_gemm_set_wait_limit(int polls)
 {
@@ -1321,11 +1342,48 @@ extern "C" int nvfp4_group_gemm_set_max_frags(int frags)
 
 namespace {
 
+// Device addresses of each device's copy of `scratch`, looked up once per
+// device (fixed-size table: the lookup path allocates nothing either).
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::atomic<int> g_scratch_cus[kMaxDevices];
+
+// The static-scratch workspace of the current device dev.
+int scratch_workspace(int dev, Workspace& out)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(NVFP4GG_UNSUPPORTED, "device index beyond the static scratch table");
+    uint8_t* ptr = g_scratch_ptr[dev].load();
+    int cus = g_scratch_cus[dev].load();
+    if (!ptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return fail(NVFP4GG_HIP_ERROR, "hipGetSymbolAddress of the static scratch failed");
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = kScratchWorkers;
+        g_scratch_cus[dev].store(cus);
+        ptr = static_cast<uint8_t*>(p);
+        g_scratch_ptr[dev].store(ptr);
+    }
+    // A launch has at most one workgroup per compute unit; the scratch holds
+    // the workspace of kScratchWorkers of them.
+    if (cus > kScratchWorkers)
+        return fail(NVFP4GG_UNSUPPORTED, "the device has " + std::to_string(cus) +
+                                             " compute units; the static scratch holds the fix-up workspace of " +
+                                             std::to_string(kScratchWorkers) + " workgroups");
+    out.partials = reinterpret_cast<float*>(ptr);
+    out.counters = reinterpret_cast<int*>(ptr + kScratchPartialBytes);
+    out.workers = cus;
+    return NVFP4GG_OK;
+}
+
 // Every grouped-GEMM entry point: fmt selects NVFP4 (E4M3 per 16 K) or
-// MXFP4 (E8M0 per 32 K), blocked_sf the blocked layout of NVFP4 scales.
+// MXFP4 (E8M0 per 32 K), blocked_sf the blocked layout of NVFP4 scales,
+// static_scratch the fix-up workspace in the static scratch (no allocation)
+// instead of the per-stream one.
 int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void* const* A_ptrs,
                     const void* const* B_ptrs, const void* const* SFA_ptrs, const void* const* SFB_ptrs,
-                    void* const* C_ptrs, void* stream, int blocked_sf, int fmt)
+                    void* const* C_ptrs, void* stream, int blocked_sf, int fmt, bool static_scratch = false)
 {
     g_last_error.clear();
     if (g <= 0) return fail(NVFP4GG_INVALID_ARG, "g must be >= 1");
@@ -1393,8 +1451,21 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         }
         if (n == 0) continue;
         if (!have_ws) {
-            const int rc = get_workspace(dev, s, ws);
-            if (rc != NVFP4GG_OK) return rc;
+            if (static_scratch) {
+                const int rc = scratch_workspace(dev, ws);
+                if (rc != NVFP4GG_OK) return rc;
+                // That memory keeps the last call's contents: the counters
+                // start from zero (a fill kernel, not a memset, so that the
+                // call can be captured into a graph).
+                hipLaunchKernelGGL(clear_counters_kernel, dim3((ws.workers + 255) / 256), dim3(256), 0, s,
+                                   ws.counters, ws.workers);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess)
+                    return fail(NVFP4GG_HIP_ERROR, std::string("kernel launch failed: ") + hipGetErrorString(e));
+            } else {
+                const int rc = get_workspace(dev, s, ws);
+                if (rc != NVFP4GG_OK) return rc;
+            }
             have_ws = true;
         }
         const int forced = g_max_frags.load();
@@ -1443,6 +1514,14 @@ extern "C" int nvfp4_group_gemm(int g, const int* M, const int* N, const int* K,
                                 void* const* C_ptrs, void* stream)
 {
     return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0, kFmtNvfp4);
+}
+
+extern "C" int nvfp4_group_gemm_noalloc(int g, const int* M, const int* N, const int* K,
+                                        const void* const* A_ptrs, const void* const* B_ptrs,
+                                        const void* const* SFA_ptrs, const void* const* SFB_ptrs,
+                                        void* const* C_ptrs, void* stream)
+{
+    return group_gemm_impl(g, M, N, K, A_ptrs, B_ptrs, SFA_ptrs, SFB_ptrs, C_ptrs, stream, 0, kFmtNvfp4, true);
 }
 
 extern "C" int nvfp4_group_gemm_blocked(int g, const int* M, const int* N, const int* K,

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version(lib):
-    assert nv.version() == 6
+    assert nv.version() == 7
 
 
 A16 = 0x10000          # fake, aligned addresses: never dereferenced, every case
