@@ -77,6 +77,11 @@ def parse():
                     help="after timing, run 3 device copies of this many MiB (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the counter-derived traffic per launch and exit (no GPU use)")
+    ap.add_argument("--counters-from", nargs="+", metavar="CSV",
+                    help="print the GEMM kernel's per-dispatch counter means from rocprofv3 "
+                         "counter_collection.csv files and exit (no GPU use)")
+    ap.add_argument("--stats-from", metavar="CSV",
+                    help="print the GEMM kernel's row of a rocprofv3 kernel_stats.csv and exit (no GPU use)")
     return ap.parse_args()
 
 
@@ -170,11 +175,26 @@ def make_device_sets(cfg, nsets, torch, blocked=False, blocked_bytes=None, fmt="
     return sets
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, target_s, fmt="nvfp4"):
-    """The oracle, as it is, on the first r_i rows of every group (all N_i
-    columns, all K_i), r_i the same fraction of M_i in each group, grown until
-    the run takes about target_s; scaled to the whole workload by
-    multiply-add count."""
+    """The oracle, as it is (plain C, -O3, OpenMP over output rows), timed on
+    a bounded sample of the workload: the first r_i rows of every group (all
+    N_i columns, all K_i), r_i the same fraction of M_i in each group, sized
+    so that one run on all host threads takes about target_s / 3.  That run
+    is repeated three times (the median is reported), and 1/threads of the
+    rows is run once on one thread.  Both are extrapolated to the whole
+    workload by multiply-add count (the oracle's cost per multiply-add does
+    not depend on which rows it computes)."""
     import oracle
     oracle.build(force=False)
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
@@ -189,27 +209,64 @@ def cpu_baseline(cfg, target_s, fmt="nvfp4"):
     total_macs = sum(m * n * k for m, n, k in zip(M, N, K))
     threads = oracle.max_threads()
 
-    def run(frac):
+    def run(frac, nthreads):
         rows = [max(1, min(M[i], int(round(M[i] * frac)))) for i in range(g)]
         A = [inputs[i][0][:rows[i]] for i in range(g)]
         SA = [inputs[i][2][:rows[i]] for i in range(g)]
         t0 = time.perf_counter()
-        run_oracle(rows, N, K, A, [x[1] for x in inputs], SA, [x[3] for x in inputs], nthreads=threads)
-        return rows, time.perf_counter() - t0
+        run_oracle(rows, N, K, A, [x[1] for x in inputs], SA, [x[3] for x in inputs], nthreads=nthreads)
+        t = time.perf_counter() - t0
+        return rows, sum(r * n * k for r, n, k in zip(rows, N, K)), t
 
+    one = target_s / 3
     frac = min(1.0, threads / max(1.0, sum(M)))
-    rows, t = run(frac)
-    while t < target_s / 4 and frac < 1.0:
+    rows, macs, t = run(frac, threads)
+    while t < one / 4 and frac < 1.0:
         frac = min(1.0, frac * 2)
-        rows, t = run(frac)
-    if t < target_s * 0.7 and frac < 1.0:
-        frac = min(1.0, frac * target_s / max(t, 1e-3))
-        rows, t = run(frac)
-    macs = sum(r * n * k for r, n, k in zip(rows, N, K))
-    us_per_call = t * 1e6 * total_macs / macs
-    return {"value": round(us_per_call, 1), "unit": "µs/call", "cores": threads, "kind": "oracle",
-            "sample": "first rows %s of the %d groups (all N, all K): %d of %d multiply-adds in %.1f s "
-                      "on %d threads, scaled to the whole workload" % (rows, g, macs, total_macs, t, threads)}
+        rows, macs, t = run(frac, threads)
+    if t < one * 0.7 and frac < 1.0:
+        frac = min(1.0, frac * one / max(t, 1e-3))
+    times = []
+    for _ in range(3):
+        rows, macs, t = run(frac, threads)
+        times.append(t)
+    t_med = float(np.median(times))
+    rows1, macs1, t1 = run(frac / threads, 1)
+    return {"value": round(t_med * 1e6 * total_macs / macs, 1), "unit": "µs/call", "cores": threads,
+            "kind": "oracle",
+            "sample": "first rows %s of the %d groups (all N, all K): %d of %d multiply-adds (%.2f%%), "
+                      "median of 3 runs on %d threads (%s s), extrapolated to the whole workload by "
+                      "multiply-add count" % (rows, g, macs, total_macs, 100.0 * macs / total_macs, threads,
+                                              ", ".join("%.2f" % x for x in times)),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(t1 * 1e6 * total_macs / macs1, 1), "unit": "µs/call",
+                              "sample": "first rows %s: %d multiply-adds in %.2f s on 1 thread, "
+                                        "extrapolated by multiply-add count" % (rows1, macs1, t1)},
+            "oracle_build": "gcc -O3 -fopenmp"}
+
+
+def counters_from(paths, kernel: str):
+    """Per-dispatch means of every counter in rocprofv3 counter_collection.csv
+    files, for the dispatches of `kernel`."""
+    out = {}
+    for path in paths:
+        acc = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        for name, vals in acc.items():
+            out[name] = {"dispatches": len(vals), "mean": sum(vals) / len(vals)}
+    return out
+
+
+def stats_from(path: str, kernel: str):
+    """The row of `kernel` in a rocprofv3 kernel_stats.csv."""
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Name"]:
+                return {k: r[k] for k in ("Name", "Calls", "AverageNs", "MinNs", "MaxNs", "StdDev") if k in r}
+    raise SystemExit("%s: no row for %s" % (path, kernel))
 
 
 def main():
@@ -218,8 +275,25 @@ def main():
         mb = args.calib_copy_mb or 512
         t = traffic_from(args.traffic_from[0], args.traffic_from[1], mb, kernel_name(args))
         total = int(round(t["FETCH_SIZE"]["bytes"] + t["WRITE_SIZE"]["bytes"]))
-        print(json.dumps({"source_sha256": source_digest(), "calib_copy_mb": mb, "counters": t,
-                          "traffic_bytes_per_launch": total}, indent=1))
+        print("source_sha256: %s" % source_digest())
+        print("calib_copy_mib: %d" % mb)
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = t[c]
+            print("%s: kernel mean %.1f KiB over %d dispatches; copy %.1f KiB; factor %.4f; %d bytes per launch"
+                  % (c, v["gemm_kib"], v["gemm_dispatches"], v["copy_kib"], v["factor"], round(v["bytes"])))
+        print("fetch_bytes_per_launch: %d" % round(t["FETCH_SIZE"]["bytes"]))
+        print("write_bytes_per_launch: %d" % round(t["WRITE_SIZE"]["bytes"]))
+        print("traffic_bytes_per_launch: %d" % total)
+        return
+    if args.counters_from:
+        print("source_sha256: %s" % source_digest())
+        for name, v in sorted(counters_from(args.counters_from, kernel_name(args)).items()):
+            print("%s: %.1f (mean of %d dispatches)" % (name, v["mean"], v["dispatches"]))
+        return
+    if args.stats_from:
+        print("source_sha256: %s" % source_digest())
+        for k, v in stats_from(args.stats_from, kernel_name(args)).items():
+            print("%s: %s" % (k, v))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
