@@ -170,12 +170,12 @@ int nvfp4_dequant_f16(int rows, int K, const void* X, const void* SFX,
  * Returns NVFP4GG_INVALID_ARG for a negative count. */
 int nvfp4_group_gemm_set_wait_limit(int polls);
 
-/* The m-block size, in fragments of 32 rows (1..6), used for every launch
+/* The m-block size, in fragments of 16 rows (1..12), used for every launch
  * (process-wide); 0 (the default) chooses it per launch from the problem
  * sizes.  Results do not depend on it beyond fp32 rounding order (each
  * output is one fp32 sum of exact products in every case); it exists for
  * tuning and so that tests can run every tile shape.  Returns
- * NVFP4GG_INVALID_ARG for a value outside 0..6. */
+ * NVFP4GG_INVALID_ARG for a value outside 0..12. */
 int nvfp4_group_gemm_set_max_frags(int frags);
 
 /* Thread-local description of the last non-OK return ("" if none). */

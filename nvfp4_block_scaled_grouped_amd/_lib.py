@@ -236,7 +236,7 @@ def set_wait_limit(polls: int):
 
 
 def set_max_frags(frags: int):
-    """m-block size (fragments of 32 rows, 1..6) forced for every launch;
+    """m-block size (fragments of 16 rows, 1..12) forced for every launch;
     0 chooses it per launch (see include/nvfp4gg.h)."""
     _check(load().nvfp4_group_gemm_set_max_frags(int(frags)))
 

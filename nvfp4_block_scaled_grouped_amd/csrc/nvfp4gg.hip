@@ -78,7 +78,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = 8;                    // two waves per SIMD
 constexpr int kThreads = kWave * kWaves;
 constexpr int kKSteps = kStageK / 32;        // MFMA k-steps per stage (32 K each)
-constexpr int kMaxAFrags = 2 * kMaxFrags;    // 16-row A fragments of a tile
+constexpr int kMaxAFrags = kMaxFrags;        // 16-row A fragments of a tile
 constexpr int kMaxChainStages = 64;          // stages one fp32 chain accumulates (8192 K)
 constexpr int kSlotFloats = kWaves * kMaxAFrags * 2 * kWave * 4;   // one partial tile
 constexpr uint32_t kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
@@ -102,7 +102,7 @@ constexpr int kWaitLimit = 1 << 20;
 #endif
 
 static_assert(kTileN == kWaves * 32, "each wave owns two 16-column B fragments");
-static_assert(kMaxFrags == 6, "the kernel instantiates m-blocks of 1 to 6 fragments");
+static_assert(kMaxFrags == 12 && kFragRows == 16, "the kernel instantiates m-blocks of 1 to 12 fragments of 16 rows");
 static_assert(kKSteps == 4, "a stage is one 16-byte piece of 4 k-steps per lane");
 
 struct GroupArgs {
@@ -259,13 +259,13 @@ __device__ __forceinline__ void stage_c(SharedMem& sm, int i, int f, const f4_t&
 // The LDS copy of the output tile to C, every global store 16 contiguous
 // bytes of a row.  Called by every thread of the workgroup once all pieces
 // are staged; the LDS is free on return.
-template <int MF>
+template <int NF>
 __device__ __forceinline__ void write_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0)
 {
     const int tid = opaque_tid();
     lds_barrier();
     const int M = ga.M, N = ga.N;
-    const int rows = M - m0 < MF * kFragRows ? M - m0 : MF * kFragRows;
+    const int rows = M - m0 < NF * kFragRows ? M - m0 : NF * kFragRows;
     const int chunk = tid % (kTileN / 8);          // 8 columns = 16 bytes
     const int n = n0 + 8 * chunk;
     const bool vec_ok = (N & 7) == 0;
@@ -284,25 +284,25 @@ __device__ __forceinline__ void write_c(SharedMem& sm, const GroupArgs& ga, int 
 }
 
 // The output tile of the workgroup from the accumulators of its waves.
-template <int MF>
+template <int NF>
 __device__ __forceinline__ void store_c(SharedMem& sm, const GroupArgs& ga, int m0, int n0,
                                         const f4_t (*acc)[2], int wave)
 {
     const int lane = opaque_tid() % kWave;
 #pragma unroll
-    for (int i = 0; i < 2 * MF; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int f = 0; f < 2; ++f) stage_c(sm, i, f, acc[i][f], wave, lane);
-    write_c<MF>(sm, ga, m0, n0);
+    write_c<NF>(sm, ga, m0, n0);
 }
 
-// One wave's fp32 block of a partial tile (2 MF x 2 x 4 floats per lane) at
+// One wave's fp32 block of a partial tile (NF x 2 x 4 floats per lane) at
 // base, in 1 KB lane-contiguous pieces.
-template <int MF>
+template <int NF>
 __device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t base, const f4_t (*acc)[2])
 {
 #pragma unroll
-    for (int i = 0; i < 2 * MF; ++i)
+    for (int i = 0; i < NF; ++i)
 #pragma unroll
         for (int f = 0; f < 2; ++f)
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i4_t, acc[i][f]), r,
@@ -312,10 +312,10 @@ __device__ __forceinline__ void store_block(__amdgpu_buffer_rsrc_t r, uint32_t b
 // acc += the block stored by store_block at base, kChunk pieces at a time
 // (the scheduling barrier keeps the loads of later chunks from being
 // hoisted, which bounds the registers in flight).
-template <int MF>
+template <int NF>
 __device__ __forceinline__ void load_block(__amdgpu_buffer_rsrc_t r, uint32_t base, f4_t (*acc)[2])
 {
-    constexpr int kPieces = 4 * MF;
+    constexpr int kPieces = 2 * NF;
     constexpr int kChunk = 12;
 #pragma unroll
     for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
@@ -387,7 +387,7 @@ __device__ __forceinline__ void phase_tail(F& f, int i, int n)
 // (partial-tile store, counter, and the fix-up by the last to arrive).
 // acc holds the wave's part of the segment's sum: acc[i][f] element r of lane
 // (c16, kq) is tile row 16 i + c16, column 32 wave + 16 f + 4 kq + r.
-template <int MF>
+template <int NF>
 __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos& pos, bool first_chain,
                                                bool last_chain, SharedMem& sm, int* s_flag, f4_t (*acc)[2],
                                                int m0, int n0, int wave)
@@ -402,9 +402,9 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     const uint32_t scratch_base =
         (uint32_t)scratch_slot(worker_id(args.G)) * kSlotFloats * 4u + ewave_in_slot;
     // Chains of one segment meet in the scratch slot.
-    if (!first_chain) load_block<MF>(rP, scratch_base, acc);
+    if (!first_chain) load_block<NF>(rP, scratch_base, acc);
     if (!last_chain) {
-        store_block<MF>(rP, scratch_base, acc);
+        store_block<NF>(rP, scratch_base, acc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         return;
     }
@@ -418,7 +418,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
     if (w_first == w_last) {
         asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
-        store_c<MF>(sm, ga, m0, n0, acc, wave);
+        store_c<NF>(sm, ga, m0, n0, acc, wave);
         return;
     }
     const int me = __builtin_amdgcn_readfirstlane(worker_id(args.G));
@@ -457,7 +457,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     const int others = w_last - w_first;
     bool fix;
     if (me != w_first) {
-        store_block<MF>(rP, slot_base(me), acc);
+        store_block<NF>(rP, slot_base(me), acc);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         if (threadIdx.x == 0) {
@@ -484,7 +484,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         fix = __builtin_amdgcn_readfirstlane(*s_flag) != 0;
         __syncthreads();
         if (!fix) {
-            store_block<MF>(rP, slot_base(me), acc);
+            store_block<NF>(rP, slot_base(me), acc);
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
             if (threadIdx.x == 0) {
@@ -502,7 +502,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     // not depend on who arrived last.  Loads carry the device-scope
     // coherence bit; a contributor index past w_last gets an offset beyond
     // the buffer, whose loads return zeros.
-    constexpr int kPieces = 4 * MF;
+    constexpr int kPieces = 2 * NF;
     auto load_piece = [&](int w, int q) {
         const uint32_t base = w <= w_last ? slot_base(w) : kNoSlot;
         return __builtin_bit_cast(
@@ -512,11 +512,11 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
         // This workgroup's partial is still in the accumulators (often the
         // case: the first contributor ends its range with the tile's first
         // stages, so it tends to finish last); the others are added to it,
-        // kChunk pieces of kBatch contributors in flight.  Tiles of 4 or more
-        // fragments take one contributor at a time (in two halves for 6
-        // fragments): their accumulators hold the registers.
-        constexpr int kChunk = MF <= 5 ? kPieces : kPieces / 2;
-        constexpr int kBatch = MF <= 3 ? 24 / kChunk : 1;
+        // kChunk pieces of kBatch contributors in flight.  Tiles of 7 or more
+        // fragments take one contributor at a time (in two halves for 11 and
+        // 12 fragments): their accumulators hold the registers.
+        constexpr int kChunk = NF <= 10 ? kPieces : kPieces / 2;
+        constexpr int kBatch = NF <= 6 ? 24 / kChunk : 1;
         for (int w0 = w_first + 1; w0 <= w_last; w0 += kBatch) {
 #pragma unroll
             for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
@@ -534,13 +534,13 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
             }
         }
         asm volatile("; fix-up, first contributor" ::: "memory");
-        store_c<MF>(sm, ga, m0, n0, acc, wave);
+        store_c<NF>(sm, ga, m0, n0, acc, wave);
     } else {
         // Every partial, this workgroup's own included, is read back, so the
         // accumulators are free: kChunk pieces of kBatch contributors in
         // flight, each summed chunk straight to the LDS copy of the tile.
-        constexpr int kChunk = MF <= 3 ? kPieces : kPieces / 2;
-        constexpr int kBatch = (MF <= 2 ? 32 : 24) / kChunk;
+        constexpr int kChunk = NF <= 6 ? kPieces : (kPieces + 1) / 2;
+        constexpr int kBatch = (NF <= 4 ? 32 : 24) / kChunk;
         const int flane = opaque_tid() % kWave;
 #pragma unroll
         for (int q0 = 0; q0 < kPieces; q0 += kChunk) {
@@ -564,14 +564,15 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
                 stage_c(sm, (q0 + q) >> 1, (q0 + q) & 1, sum[q], wave, flane);
         }
         asm volatile("; fix-up" ::: "memory");
-        write_c<MF>(sm, ga, m0, n0);
+        write_c<NF>(sm, ga, m0, n0);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
-// One chain [s_begin, s_end) of the stages of a tile with MF fragments: a
+// One chain [s_begin, s_end) of the stages of a tile of NA fragments of 16
+// rows: a
 // workgroup's segment of a tile runs as chains of at most kMaxChainStages
 // stages (one chain for any K <= 8192); first_chain / last_chain place this
 // chain in its segment.
@@ -583,9 +584,9 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
 // output columns 4 kq .. 4 kq + 3 of the 16 x 16 block.
 //
 // Waves: wave w owns columns [32 w, 32 w + 32) of the tile (B fragments
-// f = 0, 1 of 16 columns) for all 2 MF 16-row A fragments, over the whole K
+// f = 0, 1 of 16 columns) for all NA 16-row A fragments, over the whole K
 // of the chain, so every byte of B is loaded and dequantised once per tile,
-// by one wave, and one dequantised B fragment feeds 2 MF MFMAs.
+// by one wave, and one dequantised B fragment feeds NA MFMAs.
 //
 // K order within a stage (128 K, 64 bytes of a row; the sum is order-free
 // and A and B use the same order): at k-step v lane (c16, kq) holds the 8
@@ -595,7 +596,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
 // four lanes of a row read its 64 stage bytes as one contiguous run, and
 // one 16-byte load per B fragment and stage feeds all four k-steps.
 //
-// A: each stage of the tile's 2 MF fragments of 16 rows is dequantised once
+// A: each stage of the tile's NA fragments of 16 rows is dequantised once
 // by the workgroup into LDS, in operand order.  Fragment a belongs to wave
 // a % 8 (its unit a / 8), so a wave has at most two units.
 //
@@ -607,11 +608,10 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
 //     buffer, one piece per k-step of the MFMA loop, then re-loaded with
 //     stage i + 1 + kRing.
 //   * One LDS-only barrier ends the stage.
-template <int MF, bool kBlocked>
+template <int NA, bool kBlocked>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
                                             bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
-    constexpr int NA = 2 * MF;   // 16-row A fragments
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
@@ -645,9 +645,9 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         offB[f] = brow * row_bytes + 16u * kq;
     }
 
-    // This wave's A units: kU = 1 for MF <= 4, else 2 (unit x is fragment
-    // a = w + 8 x).  A unit past the tile's fragments (a >= 2 MF) loads the
-    // rows of fragment a % (2 MF) again (cache hits) and writes the discard
+    // This wave's A units: kU = 1 for NA <= 8, else 2 (unit x is fragment
+    // a = w + 8 x).  A unit past the tile's fragments (a >= NA) loads the
+    // rows of fragment a % NA again (cache hits) and writes the discard
     // area.
     constexpr int kU = NA > kWaves ? 2 : 1;
     // Register ring depth: stage i's loads go out kRing stages ahead.
@@ -870,7 +870,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
         for (; i + 3 < n; i += 4) phase_pass<0, 4, kRing>(stage, i);
         phase_tail<0, 4, kRing>(stage, i, n);
     }
-    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
+    finish_segment<NA>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
 // ------------------------------------------------------------------ MXFP4
@@ -931,11 +931,10 @@ __device__ __forceinline__ void ring_pass(F& f, int i)
 //     bytes into a double-buffered LDS stage that every wave reads.
 //   * Per stage each wave runs 2 x NA MFMAs of 16 x 16 x 128; one LDS-only
 //     barrier ends the stage.
-template <int MF>
+template <int NA>
 __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
                                                bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
-    constexpr int NA = 2 * MF;
     constexpr int kU = NA > kWaves ? 2 : 1;
     // Stages of B in flight.  Measured on MI355X: 2 beats 4 and 4 beats 8
     // on every workload (a deeper ring's first burst of loads delays every
@@ -946,7 +945,7 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     // A fragments read from LDS per group (the scheduling barrier between
     // groups keeps the compiler from loading every fragment of the stage up
     // front, which large tiles have no registers for).
-    constexpr int kAGroup = MF <= 4 ? NA : 4;
+    constexpr int kAGroup = NA <= 8 ? NA : 4;
     const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
@@ -1097,7 +1096,7 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
         for (; i + kRing - 1 < n; i += kRing) ring_pass<0, kRing>(stage, i);
         ring_tail<0, kRing>(stage, i, n);
     }
-    finish_segment<MF>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
+    finish_segment<NA>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
 // Wave-uniform values computed in vector registers (64-bit divisions have
@@ -1124,6 +1123,23 @@ __device__ __forceinline__ Pos uniform(const Pos& p)
     return r;
 }
 
+// The segment kernel of a tile of `frags` fragments (F .. kMaxFrags).
+template <bool kMx, bool kBlocked, int F>
+__device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args, const Pos& pos, int c0, int c1,
+                                               bool first, bool last, SharedMem& sm, int* s_flag)
+{
+    if constexpr (F < kMaxFrags) {
+        if (frags != F) {
+            run_segment_of<kMx, kBlocked, F + 1>(frags, args, pos, c0, c1, first, last, sm, s_flag);
+            return;
+        }
+    }
+    if constexpr (kMx)
+        run_segment_mx<F>(args, pos, c0, c1, first, last, sm, s_flag);
+    else
+        run_segment<F, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag);
+}
+
 // The persistent walk of one workgroup over its cost range: every segment
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
@@ -1143,25 +1159,7 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
         for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
             const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
             const bool first = c0 == pos.stage, last = c1 == s_end;
-            if constexpr (kMx) {
-                switch (pos.frags) {
-                    case 1: run_segment_mx<1>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 2: run_segment_mx<2>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 3: run_segment_mx<3>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 4: run_segment_mx<4>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 5: run_segment_mx<5>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    default: run_segment_mx<6>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                }
-            } else {
-                switch (pos.frags) {
-                    case 1: run_segment<1, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 2: run_segment<2, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 3: run_segment<3, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 4: run_segment<4, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    case 5: run_segment<5, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                    default: run_segment<6, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag); break;
-                }
-            }
+            run_segment_of<kMx, kBlocked, 1>(pos.frags, args, pos, c0, c1, first, last, sm, s_flag);
         }
         if (s_end < gs.stages) break;
         pos = uniform(locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages));

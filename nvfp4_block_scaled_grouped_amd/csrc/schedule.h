@@ -5,9 +5,10 @@
 // launcher include it, and a CPU test compiles it on its own.
 //
 // Terms:
-//   * fragment: 32 rows of A_i (the MFMA tile height).
+//   * fragment: 16 rows of A_i (the MFMA tile height), so a group's last
+//     fragment carries at most 15 padding rows.
 //   * m-block: up to maxf <= kMaxFrags fragments of one group, processed
-//     together (maxf is chosen per launch).  A group with F = ceil(M/32)
+//     together (maxf is chosen per launch).  A group with F = ceil(M/16)
 //     fragments has nmb = ceil(F / maxf) m-blocks; fragments are spread
 //     evenly, so the first F % nmb m-blocks get F / nmb + 1 fragments and
 //     the rest F / nmb.
@@ -19,7 +20,7 @@
 //     fragments costs unit_cost(f, fmt) units (about 50 ns of MI355X time
 //     each, fitted to measured stage times).  NVFP4 (fp16 MFMA after
 //     dequantisation): the B stream and its dequantisation do not grow with
-//     f, the MFMAs do, and tiles of more than 4 fragments give every wave a
+//     f, the MFMAs do, and tiles of more than 8 fragments give some waves a
 //     second piece of A to dequantise.  MXFP4 (native FP4 MFMA, no
 //     dequantisation): a stage is mostly its B stream.
 //   * A tile's cost range is kTileCost (the start-up and wind-down of the
@@ -40,13 +41,13 @@
 
 namespace nvfp4sched {
 
-constexpr int kMaxFrags = 6;       // fragments per m-block
-constexpr int kFragRows = 32;      // rows per fragment
+constexpr int kMaxFrags = 12;      // fragments per m-block
+constexpr int kFragRows = 16;      // rows per fragment
 constexpr int kTileN = 256;        // columns per n-block
 constexpr int kStageK = 128;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
 constexpr int kTileCost = 200;     // cost units of a tile beyond its stages
-constexpr int kMaxUnitCost = 56;   // the costliest stage (NVFP4, 6 fragments)
+constexpr int kMaxUnitCost = 56;   // the costliest stage (NVFP4, 12 fragments)
 constexpr int kFmtNvfp4 = 0;       // E4M3 scale per 16 K, fp16 MFMA
 constexpr int kFmtMxfp4 = 1;       // E8M0 scale per 32 K, FP4 MFMA
 // Least cost handed to one workgroup: keeps every workgroup range longer
@@ -57,7 +58,7 @@ static_assert(kMinUnitsPerWG >= kMaxUnitCost, "a workgroup range must hold a sta
 
 struct GroupSched {
     int64_t cost_begin;   // cost units before this group
-    int frags;            // ceil(M / 32)
+    int frags;            // ceil(M / 16)
     int mblocks;          // ceil(frags / kMaxFrags)
     int nblocks;          // ceil(N / kTileN)
     int stages;           // K / kStageK
@@ -85,12 +86,36 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
 // about 50 ns.  NVFP4: measured MI355X stage times 1.2, 1.45, 1.75, 2.3 and
-// 2.8 us for 2 to 6 fragments, one fragment extrapolated.  MXFP4: measured
-// 1.15, 1.25, 1.3 and 1.8 us for 2, 3, 4 and 5-6 fragments.
+// 2.8 us for 4, 6, 8, 10 and 12 fragments; odd counts interpolated (the
+// MFMAs grow linearly with f), 1 and 2 extrapolated.  MXFP4: measured 1.15,
+// 1.25, 1.3 and 1.8 us for 4, 6, 8 and 10-12 fragments (the step at 9:
+// every wave then stages a second A fragment).
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    if (fmt == kFmtMxfp4) return f <= 1 ? 22 : f == 2 ? 23 : f == 3 ? 25 : f == 4 ? 26 : 36;
-    return f <= 1 ? 21 : f == 2 ? 24 : f == 3 ? 29 : f == 4 ? 35 : f == 5 ? 46 : kMaxUnitCost;
+    if (fmt == kFmtMxfp4) {
+        switch (f) {
+            case 1: case 2: return 22;
+            case 3: case 4: return 23;
+            case 5: return 24;
+            case 6: return 25;
+            case 7: case 8: return 26;
+            default: return 36;
+        }
+    }
+    switch (f) {
+        case 1: return 20;
+        case 2: return 21;
+        case 3: return 23;
+        case 4: return 24;
+        case 5: return 27;
+        case 6: return 29;
+        case 7: return 32;
+        case 8: return 35;
+        case 9: return 41;
+        case 10: return 46;
+        case 11: return 51;
+        default: return kMaxUnitCost;
+    }
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.

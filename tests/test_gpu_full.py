@@ -14,9 +14,10 @@ Shapes:
     custom_kernel_fallback on page kernelbot-nvfp4-group-gemm-505431), run
     twice for bitwise determinism;
   * M = [176, 128, 248, 160], N = 8192, K = 1024 with the m-block size forced
-    to each of 1..6 fragments (so every instantiation of every kernel runs
-    its steady-state loop and its split-tile fix-up), and with the wait limit
-    0 at 4..6 fragments (the fix-up handed over to the last contributor);
+    to each of 1..12 fragments of 16 rows (so every instantiation of every
+    kernel runs its steady-state loop and its split-tile fix-up), and with
+    the wait limit 0 at 8, 11 and 12 fragments (the fix-up handed over to the
+    last contributor, in its one-contributor-at-a-time and half-tile forms);
   * a larger problem after a smaller one on one stream (the workspace is
     sized once per stream and reused).
 """
@@ -112,7 +113,7 @@ def test_workload_full(nv, oracle_lib, cfg, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("maxf", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("maxf", list(range(1, 13)))
 def test_every_mblock_size(nv, oracle_lib, maxf, fmt):
     _say("m-block size %d, %s, M=%s N=%s K=%s" % (maxf, fmt, SWEEP["M"], SWEEP["N"][0], SWEEP["K"][0]))
     dev, ref = _problem(SWEEP, fmt, oracle_lib)
@@ -125,7 +126,7 @@ def test_every_mblock_size(nv, oracle_lib, maxf, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("maxf", [4, 5, 6])
+@pytest.mark.parametrize("maxf", [8, 11, 12])
 def test_hand_over_every_large_mblock(nv, oracle_lib, maxf, fmt):
     """Wait limit 0: the first contributor of every split tile stores its
     partial and hands the fix-up over; the last to arrive sums them all."""
@@ -152,3 +153,18 @@ def test_larger_after_smaller_on_one_stream(nv, oracle_lib):
         with torch.cuda.stream(s):
             C = _run(nv, cfg, "nvfp4", dev, stream=s)
         _compare_all(C, ref, "stream reuse %s" % cfg["name"])
+
+
+LOW_M = dict(name="low_m", M=[40, 72, 164, 148, 8, 24], N=[520, 260, 1024, 300, 64, 33],
+             K=[512, 1024, 384, 768, 256, 128], seed=405)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_low_m_groups(nv, oracle_lib, fmt):
+    """Groups whose row count ends in a half-used 16-row fragment (M = 40,
+    72, 164, 148: 8, 8, 4 and 4 rows past a multiple of 32), and tiny M:
+    the last fragment's padding rows are computed from zeros and never
+    stored."""
+    _say("low M %s M=%s" % (fmt, LOW_M["M"]))
+    dev, ref = _problem(LOW_M, fmt, oracle_lib)
+    _compare_all(_run(nv, LOW_M, fmt, dev), ref, "%s low M" % fmt)
