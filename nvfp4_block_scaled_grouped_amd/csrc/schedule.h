@@ -92,30 +92,22 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 // every wave then stages a second A fragment).
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    if (fmt == kFmtMxfp4) {
-        switch (f) {
-            case 1: case 2: return 22;
-            case 3: case 4: return 23;
-            case 5: return 24;
-            case 6: return 25;
-            case 7: case 8: return 26;
-            default: return 36;
-        }
-    }
-    switch (f) {
-        case 1: return 20;
-        case 2: return 21;
-        case 3: return 23;
-        case 4: return 24;
-        case 5: return 27;
-        case 6: return 29;
-        case 7: return 32;
-        case 8: return 35;
-        case 9: return 41;
-        case 10: return 46;
-        case 11: return 51;
-        default: return kMaxUnitCost;
-    }
+    // Selects, not a switch: the kernel evaluates this per lane, where a
+    // switch becomes a chain of divergent branches.
+    if (fmt == kFmtMxfp4)
+        return f <= 2 ? 22 : f <= 4 ? 23 : f == 5 ? 24 : f == 6 ? 25 : f <= 8 ? 26 : 36;
+    return f <= 1   ? 20
+           : f == 2 ? 21
+           : f == 3 ? 23
+           : f == 4 ? 24
+           : f == 5 ? 27
+           : f == 6 ? 29
+           : f == 7 ? 32
+           : f == 8 ? 35
+           : f == 9 ? 41
+           : f == 10 ? 46
+           : f == 11 ? 51
+                     : kMaxUnitCost;
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
