@@ -181,7 +181,18 @@ struct MxStage {
     uint32_t s[kMaxAFrags][kWave];
 };
 
+// The segment a workgroup runs next (walk_range): computed by wave 0 and
+// read by every wave.
+struct WalkRec {
+    Pos pos;
+    int s_end;     // stages of the tile that start before the range's end
+    int w_first;   // the tile's first contributor
+    int w_last;    // the tile's last contributor
+    int go;        // 0: the range is done
+};
+
 struct SharedMem {
+    WalkRec walk;
     union {
         AStage a[2];
         MxStage mx[2];
@@ -392,7 +403,6 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
                                                bool last_chain, SharedMem& sm, int* s_flag, f4_t (*acc)[2],
                                                int m0, int n0, int wave)
 {
-    const GroupSched& gs = args.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const __amdgpu_buffer_rsrc_t rP =
         make_rsrc(args.partials, (uint32_t)(kSlotsPerWG * args.G) * kSlotFloats * 4u);
@@ -410,12 +420,11 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     }
 
     // Finish the tile: alone, or as one of several contributors.  Every
-    // wave holds its part of the segment's sum in acc.
-    const int unit = pos.unit;
-    const int64_t c_first = pos.tile_cost0;
-    const int64_t c_last = pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit;
-    const int w_first = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_first));
-    const int w_last = __builtin_amdgcn_readfirstlane(owner(args.W, args.G, c_last));
+    // wave holds its part of the segment's sum in acc.  The tile's
+    // contributors come from walk_range's record of this segment (rewritten
+    // only after the barriers below).
+    const int w_first = __builtin_amdgcn_readfirstlane(sm.walk.w_first);
+    const int w_last = __builtin_amdgcn_readfirstlane(sm.walk.w_last);
     if (w_first == w_last) {
         asm volatile("; whole tile" ::: "memory");   // keeps this store_c apart from the fix-up's
         store_c<NF>(sm, ga, m0, n0, acc, wave);
@@ -1143,26 +1152,51 @@ __device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args
 // The persistent walk of one workgroup over its cost range: every segment
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
+//
+// The walk's 64-bit cost arithmetic runs on the scalar unit, which all
+// waves of a CU share: done by every wave it took about 3 us per segment
+// (measured), so wave 0 alone computes each segment (its position, its end,
+// the tile's first and last contributors) and publishes it in sm.walk.
 template <bool kMx, bool kBlocked>
 __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
-    const int w = uniform(worker_id(args.G));
-    const int64_t b1 = uniform(boundary(args.W, args.G, w + 1));
-    Pos pos = uniform(locate(args.sched, args.ngroups, uniform(boundary(args.W, args.G, w))));
-    while (pos.group < args.ngroups && stage_cost(pos, pos.stage) < b1) {
-        const GroupSched& gs = args.sched[pos.group];
-        const int unit = pos.unit;
-        // Stages of this tile that start before b1.
-        const int64_t s_end64 = uniform((int64_t)((b1 - pos.tile_cost0 + unit - 1) / unit));
-        const int s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
+    const bool leader = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) == 0;
+    int64_t b1 = 0, c = 0;
+    if (leader) {
+        const int w = uniform(worker_id(args.G));
+        b1 = uniform(boundary(args.W, args.G, w + 1));
+        c = uniform(boundary(args.W, args.G, w));
+    }
+    for (;;) {
+        if (leader) {
+            WalkRec r;
+            r.pos = locate(args.sched, args.ngroups, c);
+            r.go = r.pos.group < args.ngroups && stage_cost(r.pos, r.pos.stage) < b1;
+            r.s_end = r.w_first = r.w_last = 0;
+            if (r.go) {
+                const GroupSched& gs = args.sched[r.pos.group];
+                const int unit = r.pos.unit;
+                // Stages of this tile that start before b1.
+                const int64_t s_end64 = (b1 - r.pos.tile_cost0 + unit - 1) / unit;
+                r.s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
+                r.w_first = owner(args.W, args.G, r.pos.tile_cost0);
+                r.w_last = owner(args.W, args.G, r.pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit);
+                c = uniform(r.pos.tile_cost0 + (int64_t)unit * gs.stages);   // the next tile's start
+            }
+            if (threadIdx.x == 0) sm.walk = r;
+        }
+        __syncthreads();
+        const Pos pos = uniform(sm.walk.pos);
+        const int s_end = uniform(sm.walk.s_end);
+        if (!uniform(sm.walk.go)) break;
         // The segment runs as chains of at most kMaxChainStages stages.
         for (int c0 = pos.stage; c0 < s_end; c0 += kMaxChainStages) {
             const int c1 = c0 + kMaxChainStages < s_end ? c0 + kMaxChainStages : s_end;
             const bool first = c0 == pos.stage, last = c1 == s_end;
             run_segment_of<kMx, kBlocked, 1>(pos.frags, args, pos, c0, c1, first, last, sm, s_flag);
         }
-        if (s_end < gs.stages) break;
-        pos = uniform(locate(args.sched, args.ngroups, pos.tile_cost0 + (int64_t)unit * gs.stages));
+        if (s_end < args.sched[pos.group].stages) break;
+        __syncthreads();   // every wave has read sm.walk before wave 0 rewrites it
     }
 }
 
