@@ -438,7 +438,7 @@ __device__ __forceinline__ void finish_segment(const LaunchArgs& args, const Pos
     };
     // Who finishes the tile.  The first contributor's range ends with the
     // tile's first stages and carries the tile's start-up and wind-down cost
-    // (kTileCost), so it should: it claims the fix-up and waits for the
+    // (tile_cost), so it should: it claims the fix-up and waits for the
     // others, a bounded number of polls (all workgroups of the grid run at
     // once when it fits the chip, so the others are running and never wait
     // themselves).  The others store their partials and count themselves in.

@@ -23,9 +23,9 @@
 //     f, the MFMAs do, and tiles of more than 8 fragments give some waves a
 //     second piece of A to dequantise.  MXFP4 (native FP4 MFMA, no
 //     dequantisation): a stage is mostly its B stream.
-//   * A tile's cost range is kTileCost (the start-up and wind-down of the
-//     segment that starts it: first loads, partial-tile stores, the fix-up)
-//     followed by its stages.
+//   * A tile's cost range is tile_cost(f) (the start-up and wind-down of
+//     the segment that starts it: first loads, the fix-up, the output
+//     store) followed by its stages.
 //   * Workgroup w of G takes the cost range [w*W/G, (w+1)*W/G), rounded up
 //     to stage starts, so every stage belongs to exactly one workgroup.
 #ifndef NVFP4GG_SCHEDULE_H
@@ -46,7 +46,21 @@ constexpr int kFragRows = 16;      // rows per fragment
 constexpr int kTileN = 256;        // columns per n-block
 constexpr int kStageK = 128;       // K per stage
 constexpr int kMaxGroups = 32;     // groups per launch
-constexpr int kTileCost = 200;     // cost units of a tile beyond its stages
+#ifndef NVFP4_TILE_COST_BASE
+#define NVFP4_TILE_COST_BASE 40
+#endif
+#ifndef NVFP4_TILE_COST_PER_FRAG
+#define NVFP4_TILE_COST_PER_FRAG 25
+#endif
+// Cost units of a tile of f fragments beyond its stages: tile_cost(f).  It
+// is carried by the tile's first contributor, which starts the tile and
+// finishes it (waits for the others, reads their partial tiles of 16 f
+// rows each and stores C): that part grows with the tile's rows.  Swept on
+// MI355X over the five workloads (flat 100 to 300, and 0 to 60 plus 15 to
+// 45 per fragment); 40 + 25 f beat the flat 200 on every workload (c4 by
+// 1.6 us, c2 by 1.3 us, c5 by about 2 us).
+constexpr int kTileCostBase = NVFP4_TILE_COST_BASE;
+constexpr int kTileCostPerFrag = NVFP4_TILE_COST_PER_FRAG;
 constexpr int kMaxUnitCost = 56;   // the costliest stage (NVFP4, 12 fragments)
 constexpr int kFmtNvfp4 = 0;       // E4M3 scale per 16 K, fp16 MFMA
 constexpr int kFmtMxfp4 = 1;       // E8M0 scale per 32 K, FP4 MFMA
@@ -90,6 +104,8 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 // MFMAs grow linearly with f), 1 and 2 extrapolated.  MXFP4: measured 1.15,
 // 1.25, 1.3 and 1.8 us for 4, 6, 8 and 10-12 fragments (the step at 9:
 // every wave then stages a second A fragment).
+NVFP4_HD int tile_cost(int f) { return kTileCostBase + kTileCostPerFrag * f; }
+
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
     // Selects, not a switch: the kernel evaluates this per lane, where a
@@ -124,15 +140,16 @@ NVFP4_HD int mblock_first_frag(int F, int nmb, int i)
     return i * base + (i < extra ? i : extra);
 }
 
-// Cost before m-block i of a column (i <= mblocks): i tiles of kTileCost
-// plus their stages.
+// Cost before m-block i of a column (i <= mblocks): i tiles, each its
+// tile_cost plus its stages.
 NVFP4_HD int64_t mblock_cost0(const GroupSched& g, int i)
 {
     const int base = g.frags / g.mblocks, extra = g.frags % g.mblocks;
     const int big = i < extra ? i : extra;             // m-blocks of base + 1 fragments before i
     const int64_t stage_sum =
         (int64_t)(i - big) * unit_cost(base, g.fmt) + (int64_t)big * unit_cost(base + 1, g.fmt);
-    return (int64_t)kTileCost * i + stage_sum * g.stages;
+    const int64_t tile_sum = (int64_t)(i - big) * tile_cost(base) + (int64_t)big * tile_cost(base + 1);
+    return tile_sum + stage_sum * g.stages;
 }
 
 // Cost of one n-block column of a group (all m-blocks, all stages).
@@ -176,9 +193,9 @@ NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
         r.frags = mblock_frags(g.frags, g.mblocks, mb);
         r.unit = unit_cost(r.frags, g.fmt);
         const int64_t mcost0 = mblock_cost0(g, mb);
-        q -= mcost0 + kTileCost;   // relative to the start of stage 0
+        q -= mcost0 + tile_cost(r.frags);   // relative to the start of stage 0
         r.stage = q <= 0 ? 0 : (int)((q + r.unit - 1) / r.unit);
-        r.tile_cost0 = g.cost_begin + (int64_t)r.nb * cc + mcost0 + kTileCost;
+        r.tile_cost0 = g.cost_begin + (int64_t)r.nb * cc + mcost0 + tile_cost(r.frags);
         if (r.stage < g.stages) return r;
         p = r.tile_cost0 + (int64_t)r.unit * g.stages;   // rounded past the tile: next tile
     }

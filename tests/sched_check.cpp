@@ -45,7 +45,8 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
         for (int b = 0; b <= gs[i].mblocks; ++b) {
             CHECK(mblock_cost0(gs[i], b) == c, "mblock_cost0 group %d block %d", i, b);
             if (b < gs[i].mblocks)
-                c += kTileCost + (int64_t)gs[i].stages * unit_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b), fmt);
+                c += tile_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b)) +
+                     (int64_t)gs[i].stages * unit_cost(mblock_frags(gs[i].frags, gs[i].mblocks, b), fmt);
         }
     }
     const int64_t W = cost;
