@@ -184,6 +184,8 @@ struct MxStage {
 // The segment a workgroup runs next (walk_range): computed by wave 0 and
 // read by every wave.
 struct WalkRec {
+    int next;      // wave 0's walk: the next segment's cost position
+    int end;       // wave 0's walk: the range's end
     Pos pos;
     int s_end;     // stages of the tile that start before the range's end
     int w_first;   // the tile's first contributor
@@ -1149,6 +1151,28 @@ __device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args
         run_segment<F, kBlocked>(args, pos, c0, c1, first, last, sm, s_flag);
 }
 
+// Wave 0's step of the walk: the segment that starts at cost position c in
+// a range ending at b1, and c moved to the tile after it, in C arithmetic.
+template <typename C>
+__device__ __forceinline__ void walk_step(const LaunchArgs& args, C& c, C b1, WalkRec& r)
+{
+    const C W = (C)args.W, b1c = (C)b1;
+    r.pos = locate<C>(args.sched, args.ngroups, (C)c);
+    const C t0 = (C)r.pos.tile_cost0;
+    const int unit = r.pos.unit;
+    r.go = r.pos.group < args.ngroups && t0 + (C)r.pos.stage * unit < b1c;
+    r.s_end = r.w_first = r.w_last = 0;
+    if (r.go) {
+        const int stages = args.sched[r.pos.group].stages;
+        // Stages of this tile that start before b1.
+        const C s_end = (b1c - t0 + unit - 1) / unit;
+        r.s_end = s_end < (C)stages ? (int)s_end : stages;
+        r.w_first = owner<C>(W, args.G, t0);
+        r.w_last = owner<C>(W, args.G, t0 + (C)(stages - 1) * unit);
+        c = t0 + (C)unit * stages;   // the next tile's start
+    }
+}
+
 // The persistent walk of one workgroup over its cost range: every segment
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
@@ -1160,29 +1184,29 @@ __device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args
 template <bool kMx, bool kBlocked>
 __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
+    // The cost arithmetic is 32-bit (the host keeps the total cost below
+    // kMaxLaunchCost).  Wave 0's walk state (the next position and the
+    // range's end) lives in LDS between segments, so no register holds it
+    // through a segment.
     const bool leader = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) == 0;
-    int64_t b1 = 0, c = 0;
     if (leader) {
         const int w = uniform(worker_id(args.G));
-        b1 = uniform(boundary(args.W, args.G, w + 1));
-        c = uniform(boundary(args.W, args.G, w));
+        const int32_t W = (int32_t)uniform(args.W);
+        const int32_t b1 = boundary<int32_t>(W, args.G, w + 1);
+        const int32_t c = boundary<int32_t>(W, args.G, w);
+        if (threadIdx.x == 0) {
+            sm.walk.next = c;
+            sm.walk.end = b1;
+        }
     }
     for (;;) {
         if (leader) {
             WalkRec r;
-            r.pos = locate(args.sched, args.ngroups, c);
-            r.go = r.pos.group < args.ngroups && stage_cost(r.pos, r.pos.stage) < b1;
-            r.s_end = r.w_first = r.w_last = 0;
-            if (r.go) {
-                const GroupSched& gs = args.sched[r.pos.group];
-                const int unit = r.pos.unit;
-                // Stages of this tile that start before b1.
-                const int64_t s_end64 = (b1 - r.pos.tile_cost0 + unit - 1) / unit;
-                r.s_end = s_end64 < gs.stages ? (int)s_end64 : gs.stages;
-                r.w_first = owner(args.W, args.G, r.pos.tile_cost0);
-                r.w_last = owner(args.W, args.G, r.pos.tile_cost0 + (int64_t)(gs.stages - 1) * unit);
-                c = uniform(r.pos.tile_cost0 + (int64_t)unit * gs.stages);   // the next tile's start
-            }
+            int32_t c = uniform(sm.walk.next);
+            const int32_t b1 = uniform(sm.walk.end);
+            walk_step<int32_t>(args, c, b1, r);
+            r.next = c;
+            r.end = b1;
             if (threadIdx.x == 0) sm.walk = r;
         }
         __syncthreads();
@@ -1524,6 +1548,8 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         args.blocked_sf = blocked_sf;
         args.W = cost;
         args.G = grid_size(cost, ws.workers);
+        if (cost > kMaxLaunchCost)
+            return fail(NVFP4GG_UNSUPPORTED, "launch too large: its schedule cost exceeds 2^31 units");
         args.partials = ws.partials;
         args.counters = ws.counters;
         const void* kernel = fmt == kFmtMxfp4 ? reinterpret_cast<const void*>(&mxfp4_group_gemm_kernel)

@@ -108,22 +108,17 @@ NVFP4_HD int tile_cost(int f) { return kTileCostBase + kTileCostPerFrag * f; }
 
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
 {
-    // Selects, not a switch: the kernel evaluates this per lane, where a
-    // switch becomes a chain of divergent branches.
-    if (fmt == kFmtMxfp4)
-        return f <= 2 ? 22 : f <= 4 ? 23 : f == 5 ? 24 : f == 6 ? 25 : f <= 8 ? 26 : 36;
-    return f <= 1   ? 20
-           : f == 2 ? 21
-           : f == 3 ? 23
-           : f == 4 ? 24
-           : f == 5 ? 27
-           : f == 6 ? 29
-           : f == 7 ? 32
-           : f == 8 ? 35
-           : f == 9 ? 41
-           : f == 10 ? 46
-           : f == 11 ? 51
-                     : kMaxUnitCost;
+    // One byte per fragment count (1..8 in the first word, 9..12 in the
+    // second), read with a select, a shift and a mask: the kernel evaluates
+    // this many times per walk, where a chain of comparisons compiles to a
+    // chain of branches (measured: about 2 us per walk).
+    //            f =   8  7  6  5  4  3  2  1                 12 11 10  9
+    // NVFP4:          35 32 29 27 24 23 21 20                 56 51 46 41
+    // MXFP4:          26 26 25 24 23 23 22 22                 36 36 36 36
+    const bool mx = fmt == kFmtMxfp4;
+    const uint64_t word = f <= 8 ? (mx ? 0x1a1a191817171616ull : 0x23201d1b18171514ull) : (mx ? 0x0000000024242424ull : 0x0000000038332e29ull);
+    const int i = (f <= 1 ? 0 : f > kMaxFrags ? kMaxFrags - 1 : f - 1) & 7;
+    return (int)((word >> (8 * i)) & 0xFF);
 }
 
 // Fragments of m-block i of a group with F fragments in nmb m-blocks.
@@ -140,22 +135,32 @@ NVFP4_HD int mblock_first_frag(int F, int nmb, int i)
     return i * base + (i < extra ? i : extra);
 }
 
+// Cost positions are int64_t on the host.  The functions below take the
+// cost type C as a parameter: the kernel walks the schedule in int32_t (the
+// host keeps a launch's total cost below kMaxLaunchCost, and no product of
+// a cost and a workgroup count is formed), because the GPU's scalar unit
+// has no 64-bit less-than: 64-bit cost comparisons become vector compares
+// and branches on their result (measured: about 2 us per walk).
+constexpr int64_t kMaxLaunchCost = ((int64_t)1 << 31) - 1;
+
 // Cost before m-block i of a column (i <= mblocks): i tiles, each its
 // tile_cost plus its stages.
-NVFP4_HD int64_t mblock_cost0(const GroupSched& g, int i)
+template <typename C = int64_t>
+NVFP4_HD C mblock_cost0(const GroupSched& g, int i)
 {
     const int base = g.frags / g.mblocks, extra = g.frags % g.mblocks;
     const int big = i < extra ? i : extra;             // m-blocks of base + 1 fragments before i
-    const int64_t stage_sum =
-        (int64_t)(i - big) * unit_cost(base, g.fmt) + (int64_t)big * unit_cost(base + 1, g.fmt);
-    const int64_t tile_sum = (int64_t)(i - big) * tile_cost(base) + (int64_t)big * tile_cost(base + 1);
+    const C stage_sum = (C)(i - big) * unit_cost(base, g.fmt) + (C)big * unit_cost(base + 1, g.fmt);
+    const C tile_sum = (C)(i - big) * tile_cost(base) + (C)big * tile_cost(base + 1);
     return tile_sum + stage_sum * g.stages;
 }
 
 // Cost of one n-block column of a group (all m-blocks, all stages).
-NVFP4_HD int64_t column_cost(const GroupSched& g) { return mblock_cost0(g, g.mblocks); }
+template <typename C = int64_t>
+NVFP4_HD C column_cost(const GroupSched& g) { return mblock_cost0<C>(g, g.mblocks); }
 
-NVFP4_HD int64_t group_cost(const GroupSched& g) { return column_cost(g) * g.nblocks; }
+template <typename C = int64_t>
+NVFP4_HD C group_cost(const GroupSched& g) { return column_cost<C>(g) * g.nblocks; }
 
 // A unit position: tile (group, n-block, m-block) and stage.
 struct Pos {
@@ -168,36 +173,39 @@ struct Pos {
 // The stage-aligned position of cost point p: the first stage that starts at
 // or after p.  Every group must have cost > 0 (the host launches no empty
 // group).  For p >= the total cost the result has group == ngroups.
-NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, int64_t p)
+template <typename C = int64_t>
+NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, C p)
 {
     Pos r;
     for (;;) {
         int gi = 0;
-        while (gi + 1 < ngroups && gs[gi + 1].cost_begin <= p) ++gi;
+        while (gi + 1 < ngroups && (C)gs[gi + 1].cost_begin <= p) ++gi;
         const GroupSched& g = gs[gi];
-        int64_t q = p - g.cost_begin;
-        if (q >= group_cost(g)) {
+        const C cb = (C)g.cost_begin;
+        C q = p - cb;
+        if (q >= group_cost<C>(g)) {
             r.group = ngroups;
             r.nb = r.mb = r.stage = r.frags = 0;
             r.unit = 1;
             r.tile_cost0 = p;
             return r;
         }
-        const int64_t cc = column_cost(g);
+        const C cc = column_cost<C>(g);
         r.group = gi;
         r.nb = (int)(q / cc);
-        q -= (int64_t)r.nb * cc;
+        q -= (C)r.nb * cc;
         int mb = 0;
-        while (mb + 1 < g.mblocks && mblock_cost0(g, mb + 1) <= q) ++mb;
+        while (mb + 1 < g.mblocks && mblock_cost0<C>(g, mb + 1) <= q) ++mb;
         r.mb = mb;
         r.frags = mblock_frags(g.frags, g.mblocks, mb);
         r.unit = unit_cost(r.frags, g.fmt);
-        const int64_t mcost0 = mblock_cost0(g, mb);
+        const C mcost0 = mblock_cost0<C>(g, mb);
         q -= mcost0 + tile_cost(r.frags);   // relative to the start of stage 0
         r.stage = q <= 0 ? 0 : (int)((q + r.unit - 1) / r.unit);
-        r.tile_cost0 = g.cost_begin + (int64_t)r.nb * cc + mcost0 + tile_cost(r.frags);
+        const C t0 = cb + (C)r.nb * cc + mcost0 + tile_cost(r.frags);
+        r.tile_cost0 = t0;
         if (r.stage < g.stages) return r;
-        p = r.tile_cost0 + (int64_t)r.unit * g.stages;   // rounded past the tile: next tile
+        p = t0 + (C)r.unit * g.stages;   // rounded past the tile: next tile
     }
 }
 
@@ -259,18 +267,26 @@ inline int choose_max_frags(int n, const int* M, const int* N, const int* K, int
     return best;
 }
 
-// Workgroup boundary b_w = floor(w * W / G) (w = 0..G).
-NVFP4_HD int64_t boundary(int64_t W, int G, int w) { return (W * (int64_t)w) / G; }
+// Workgroup boundary b_w = floor(w * W / G) (w = 0..G), as
+// (W / G) w + ((W % G) w) / G, which never forms W w.
+template <typename C = int64_t>
+NVFP4_HD C boundary(C W, int G, int w)
+{
+    return (W / G) * (C)w + ((W % G) * (C)w) / G;
+}
 
 // The workgroup that owns the stage starting at cost position c
-// (the largest w with b_w <= c).
-NVFP4_HD int owner(int64_t W, int G, int64_t c)
+// (the largest w with b_w <= c): a float estimate of c G / W (off by at
+// most one for G <= 512), corrected exactly against boundary().
+template <typename C = int64_t>
+NVFP4_HD int owner(C W, int G, C c)
 {
-    int64_t w = (c * G + G - 1) / W;
+    int w = (int)((float)c * (float)G / (float)W);
     if (w > G - 1) w = G - 1;
-    while (w > 0 && boundary(W, G, (int)w) > c) --w;
-    while (w + 1 < G && boundary(W, G, (int)w + 1) <= c) ++w;
-    return (int)w;
+    if (w < 0) w = 0;
+    while (w > 0 && boundary<C>(W, G, w) > c) --w;
+    while (w + 1 < G && boundary<C>(W, G, w + 1) <= c) ++w;
+    return w;
 }
 
 // Workspace slots of workgroup w (one fp32 partial tile each): a tile split

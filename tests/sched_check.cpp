@@ -99,6 +99,15 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
                 CHECK(slot != scratch_slot(w), "partial in the scratch slot");
                 CHECK(slot < kSlotsPerWG * G, "slot bound");
             }
+            if (W <= kMaxLaunchCost) {
+                // the kernel's 32-bit walk finds the same segment and contributors
+                const Pos p32 = locate<int32_t>(gs, ng, (int32_t)pos.tile_cost0 + (int32_t)pos.stage * unit);
+                CHECK(p32.group == pos.group && p32.nb == pos.nb && p32.mb == pos.mb && p32.stage == pos.stage &&
+                          p32.tile_cost0 == pos.tile_cost0 && p32.unit == pos.unit, "32-bit locate w=%d", w);
+                CHECK(owner<int32_t>((int32_t)W, G, (int32_t)c_first) == wf &&
+                          owner<int32_t>((int32_t)W, G, (int32_t)c_last) == wl, "32-bit owner w=%d", w);
+                CHECK(boundary<int32_t>((int32_t)W, G, w + 1) == b1, "32-bit boundary w=%d", w);
+            }
             if (s_end < g.stages) break;
             pos = locate(gs, ng, pos.tile_cost0 + (int64_t)unit * g.stages);
         }
