@@ -195,6 +195,9 @@ struct WalkRec {
 
 struct SharedMem {
     WalkRec walk;
+    // The launch's group table, copied from the kernel arguments at entry
+    // (walk_range): the walk and the segments read it from here.
+    GroupSched sched[kMaxGroups];
     union {
         AStage a[2];
         MxStage mx[2];
@@ -623,7 +626,7 @@ template <int NA, bool kBlocked>
 __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& pos, int s_begin, int s_end,
                                             bool first_chain, bool last_chain, SharedMem& sm, int* s_flag)
 {
-    const GroupSched& gs = args.sched[pos.group];
+    const GroupSched& gs = sm.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
@@ -631,7 +634,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
     const int c16 = lane & 15;
     const int kq = lane >> 4;
     const int M = ga.M, N = ga.N, K = ga.K;
-    const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
+    const int m0 = mblock_first_frag(__builtin_amdgcn_readfirstlane(gs.frags), __builtin_amdgcn_readfirstlane(gs.mblocks), pos.mb) * kFragRows;
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 16;
@@ -957,7 +960,7 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     // groups keeps the compiler from loading every fragment of the stage up
     // front, which large tiles have no registers for).
     constexpr int kAGroup = NA <= 8 ? NA : 4;
-    const GroupSched& gs = args.sched[pos.group];
+    const GroupSched& gs = sm.sched[pos.group];
     const GroupArgs& ga = args.grp[pos.group];
     const int tid = opaque_tid();
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -965,7 +968,7 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     const int c16 = lane & 15;
     const int kq = lane >> 4;
     const int M = ga.M, N = ga.N, K = ga.K;
-    const int m0 = mblock_first_frag(gs.frags, gs.mblocks, pos.mb) * kFragRows;
+    const int m0 = mblock_first_frag(__builtin_amdgcn_readfirstlane(gs.frags), __builtin_amdgcn_readfirstlane(gs.mblocks), pos.mb) * kFragRows;
     const int n0 = pos.nb * kTileN;
     const uint32_t row_bytes = (uint32_t)K / 2;
     const uint32_t row_scales = (uint32_t)K / 32;
@@ -1153,17 +1156,18 @@ __device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args
 
 // Wave 0's step of the walk: the segment that starts at cost position c in
 // a range ending at b1, and c moved to the tile after it, in C arithmetic.
+// gs is the LDS copy of the group table.
 template <typename C>
-__device__ __forceinline__ void walk_step(const LaunchArgs& args, C& c, C b1, WalkRec& r)
+__device__ __forceinline__ void walk_step(const LaunchArgs& args, const GroupSched* gs, C& c, C b1, WalkRec& r)
 {
     const C W = (C)args.W, b1c = (C)b1;
-    r.pos = locate<C>(args.sched, args.ngroups, (C)c);
+    r.pos = locate<C>(gs, args.ngroups, (C)c);
     const C t0 = (C)r.pos.tile_cost0;
     const int unit = r.pos.unit;
     r.go = r.pos.group < args.ngroups && t0 + (C)r.pos.stage * unit < b1c;
     r.s_end = r.w_first = r.w_last = 0;
     if (r.go) {
-        const int stages = args.sched[r.pos.group].stages;
+        const int stages = uniform(gs[r.pos.group].stages);
         // Stages of this tile that start before b1.
         const C s_end = (b1c - t0 + unit - 1) / unit;
         r.s_end = s_end < (C)stages ? (int)s_end : stages;
@@ -1188,23 +1192,37 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
     // kMaxLaunchCost).  Wave 0's walk state (the next position and the
     // range's end) lives in LDS between segments, so no register holds it
     // through a segment.
+    // The group table goes to LDS with one 16-byte load per lane, issued
+    // before anything waits for the scalar loads of W and G: its lines then
+    // arrive in the same memory round trip as those, where the walk's scan of
+    // the table in kernel-argument memory would wait for one cold line after
+    // another.
+    static_assert(sizeof(GroupSched) * kMaxGroups == kWave * 16, "the group table is one 16-byte piece per lane");
+    const int tlane = opaque_tid() % kWave;
+    const i4_t table = reinterpret_cast<const i4_t*>(args.sched)[tlane];
+    __builtin_amdgcn_sched_barrier(0);
     const bool leader = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) == 0;
     if (leader) {
-        const int w = uniform(worker_id(args.G));
-        const int32_t W = (int32_t)uniform(args.W);
-        const int32_t b1 = boundary<int32_t>(W, args.G, w + 1);
-        const int32_t c = boundary<int32_t>(W, args.G, w);
+        // W (below 2^31, checked by the host) and G, loaded together (the
+        // empty asm takes both, so neither load sinks below the other's use).
+        int G = args.G;
+        int32_t W = (int32_t)args.W;
+        asm volatile("" : "+s"(G), "+s"(W));
+        const int w = uniform(worker_id(G));
+        const int32_t b1 = boundary<int32_t>(W, G, w + 1);
+        const int32_t c = boundary<int32_t>(W, G, w);
         if (threadIdx.x == 0) {
             sm.walk.next = c;
             sm.walk.end = b1;
         }
+        reinterpret_cast<i4_t*>(sm.sched)[tlane] = table;
     }
     for (;;) {
         if (leader) {
             WalkRec r;
             int32_t c = uniform(sm.walk.next);
             const int32_t b1 = uniform(sm.walk.end);
-            walk_step<int32_t>(args, c, b1, r);
+            walk_step<int32_t>(args, sm.sched, c, b1, r);
             r.next = c;
             r.end = b1;
             if (threadIdx.x == 0) sm.walk = r;
@@ -1219,7 +1237,7 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
             const bool first = c0 == pos.stage, last = c1 == s_end;
             run_segment_of<kMx, kBlocked, 1>(pos.frags, args, pos, c0, c1, first, last, sm, s_flag);
         }
-        if (s_end < args.sched[pos.group].stages) break;
+        if (s_end < uniform(sm.sched[pos.group].stages)) break;
         __syncthreads();   // every wave has read sm.walk before wave 0 rewrites it
     }
 }
