@@ -125,6 +125,7 @@ struct LaunchArgs {
     int ngroups;
     int blocked_sf;       // scales in the blocked (128 x 4 atom) layout, else row-major
     int wait_limit;       // polls of a tile's first contributor waiting for the others
+    Bounds bounds;        // the workgroup boundaries of W over G (schedule.h)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes)
@@ -1155,25 +1156,31 @@ __device__ __forceinline__ void run_segment_of(int frags, const LaunchArgs& args
 }
 
 // Wave 0's step of the walk: the segment that starts at cost position c in
-// a range ending at b1, and c moved to the tile after it, in C arithmetic.
-// gs is the LDS copy of the group table.
-template <typename C>
-__device__ __forceinline__ void walk_step(const LaunchArgs& args, const GroupSched* gs, C& c, C b1, WalkRec& r)
+// a range ending at b1, and c moved to the tile after it.  gs is the LDS
+// copy of the group table.  The group of c comes from one LDS read per lane
+// and a ballot (so locate scans no further), and the tile's contributors
+// from owner_b, whose boundaries take no division.
+__device__ __forceinline__ void walk_step(const LaunchArgs& args, const GroupSched* gs, int32_t& c, int32_t b1,
+                                          WalkRec& r)
 {
-    const C W = (C)args.W, b1c = (C)b1;
-    r.pos = locate<C>(gs, args.ngroups, (C)c);
-    const C t0 = (C)r.pos.tile_cost0;
+    const int ng = args.ngroups;
+    const int lane = opaque_tid() % kWave;
+    const int32_t cb = lane < kMaxGroups ? (int32_t)gs[lane].cost_begin : 0;
+    const int gi = __builtin_popcountll(__ballot(lane >= 1 && lane < ng && cb <= c));
+    r.pos = locate<int32_t>(gs, ng, c, gi);
+    const int32_t t0 = (int32_t)r.pos.tile_cost0;
     const int unit = r.pos.unit;
-    r.go = r.pos.group < args.ngroups && t0 + (C)r.pos.stage * unit < b1c;
+    r.go = r.pos.group < ng && t0 + r.pos.stage * unit < b1;
     r.s_end = r.w_first = r.w_last = 0;
     if (r.go) {
         const int stages = uniform(gs[r.pos.group].stages);
         // Stages of this tile that start before b1.
-        const C s_end = (b1c - t0 + unit - 1) / unit;
-        r.s_end = s_end < (C)stages ? (int)s_end : stages;
-        r.w_first = owner<C>(W, args.G, t0);
-        r.w_last = owner<C>(W, args.G, t0 + (C)(stages - 1) * unit);
-        c = t0 + (C)unit * stages;   // the next tile's start
+        const int32_t s_end = (b1 - t0 + unit - 1) / unit;
+        r.s_end = s_end < stages ? s_end : stages;
+        const int32_t W = (int32_t)args.W;
+        r.w_first = owner_b(args.bounds, W, t0);
+        r.w_last = owner_b(args.bounds, W, t0 + (stages - 1) * unit);
+        c = t0 + unit * stages;   // the next tile's start
     }
 }
 
@@ -1203,14 +1210,14 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
     __builtin_amdgcn_sched_barrier(0);
     const bool leader = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave) == 0;
     if (leader) {
-        // W (below 2^31, checked by the host) and G, loaded together (the
-        // empty asm takes both, so neither load sinks below the other's use).
-        int G = args.G;
-        int32_t W = (int32_t)args.W;
-        asm volatile("" : "+s"(G), "+s"(W));
-        const int w = uniform(worker_id(G));
-        const int32_t b1 = boundary<int32_t>(W, G, w + 1);
-        const int32_t c = boundary<int32_t>(W, G, w);
+        // The boundaries of W (below 2^31, checked by the host) over G,
+        // loaded together (the empty asm takes every field, so no load sinks
+        // below another's use).
+        Bounds bd = args.bounds;
+        asm volatile("" : "+s"(bd.q), "+s"(bd.r), "+s"(bd.R), "+s"(bd.G));
+        const int w = uniform(worker_id(bd.G));
+        const int32_t b1 = bound_at(bd, w + 1);
+        const int32_t c = bound_at(bd, w);
         if (threadIdx.x == 0) {
             sm.walk.next = c;
             sm.walk.end = b1;
@@ -1222,7 +1229,7 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
             WalkRec r;
             int32_t c = uniform(sm.walk.next);
             const int32_t b1 = uniform(sm.walk.end);
-            walk_step<int32_t>(args, sm.sched, c, b1, r);
+            walk_step(args, sm.sched, c, b1, r);
             r.next = c;
             r.end = b1;
             if (threadIdx.x == 0) sm.walk = r;
@@ -1568,6 +1575,9 @@ int group_gemm_impl(int g, const int* M, const int* N, const int* K, const void*
         args.G = grid_size(cost, ws.workers);
         if (cost > kMaxLaunchCost)
             return fail(NVFP4GG_UNSUPPORTED, "launch too large: its schedule cost exceeds 2^31 units");
+        if (args.G > kMaxBoundsG)
+            return fail(NVFP4GG_UNSUPPORTED, "more workgroups than the schedule's boundary arithmetic supports");
+        args.bounds = make_bounds(cost, args.G);
         args.partials = ws.partials;
         args.counters = ws.counters;
         const void* kernel = fmt == kFmtMxfp4 ? reinterpret_cast<const void*>(&mxfp4_group_gemm_kernel)

@@ -173,12 +173,13 @@ struct Pos {
 // The stage-aligned position of cost point p: the first stage that starts at
 // or after p.  Every group must have cost > 0 (the host launches no empty
 // group).  For p >= the total cost the result has group == ngroups.
+// gi0 may name any group at or before p's group (the scan starts there).
 template <typename C = int64_t>
-NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, C p)
+NVFP4_HD Pos locate(const GroupSched* gs, int ngroups, C p, int gi0 = 0)
 {
     Pos r;
+    int gi = gi0;   // p only grows below, so the scan resumes where it stopped
     for (;;) {
-        int gi = 0;
         while (gi + 1 < ngroups && (C)gs[gi + 1].cost_begin <= p) ++gi;
         const GroupSched& g = gs[gi];
         const C cb = (C)g.cost_begin;
@@ -286,6 +287,49 @@ NVFP4_HD int owner(C W, int G, C c)
     if (w < 0) w = 0;
     while (w > 0 && boundary<C>(W, G, w) > c) --w;
     while (w + 1 < G && boundary<C>(W, G, w + 1) <= c) ++w;
+    return w;
+}
+
+// The boundaries of one launch without a division (the kernel's walk):
+// b_w = q w + floor(r w / G) with q = W / G, r = W % G, and the last
+// quotient as the high word of (r w) R, R = ceil(2^32 / G).  That is exact:
+// R G = 2^32 + e with 0 <= e < G, so (r w) R / 2^32 exceeds (r w) / G by
+// (r w) e / (G 2^32) < G^2 / 2^32, below 1 / G (the least distance from
+// (r w) / G up to the next integer) while G^3 < 2^32.  Valid for
+// W <= kMaxLaunchCost and 1 <= G <= kMaxBoundsG.
+constexpr int kMaxBoundsG = 1024;
+struct Bounds {
+    int32_t q;    // W / G
+    int32_t r;    // W % G
+    uint32_t R;   // ceil(2^32 / G); unused (0) for G = 1, where r = 0
+    int32_t G;
+};
+
+inline Bounds make_bounds(int64_t W, int G)
+{
+    Bounds b;
+    b.q = (int32_t)(W / G);
+    b.r = (int32_t)(W % G);
+    b.R = G > 1 ? (uint32_t)((((uint64_t)1 << 32) + (uint64_t)G - 1) / (uint64_t)G) : 0u;
+    b.G = G;
+    return b;
+}
+
+NVFP4_HD int32_t bound_at(const Bounds& b, int w)
+{
+    const uint32_t t = (uint32_t)b.r * (uint32_t)w;   // < G^2
+    return b.q * w + (int32_t)(((uint64_t)t * b.R) >> 32);
+}
+
+// owner() on Bounds: the same float estimate, corrected against bound_at().
+NVFP4_HD int owner_b(const Bounds& b, int32_t W, int32_t c)
+{
+    const int G = b.G;
+    int w = (int)((float)c * (float)G / (float)W);
+    if (w > G - 1) w = G - 1;
+    if (w < 0) w = 0;
+    while (w > 0 && bound_at(b, w) > c) --w;
+    while (w + 1 < G && bound_at(b, w + 1) <= c) ++w;
     return w;
 }
 

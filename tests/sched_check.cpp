@@ -107,6 +107,18 @@ static void run_case(const std::vector<int>& M, const std::vector<int>& N, const
                 CHECK(owner<int32_t>((int32_t)W, G, (int32_t)c_first) == wf &&
                           owner<int32_t>((int32_t)W, G, (int32_t)c_last) == wl, "32-bit owner w=%d", w);
                 CHECK(boundary<int32_t>((int32_t)W, G, w + 1) == b1, "32-bit boundary w=%d", w);
+                // the kernel's walk: division-free boundaries and owners, and
+                // locate started at the group a ballot over the table counts
+                const Bounds bd = make_bounds(W, G);
+                CHECK(bound_at(bd, w + 1) == b1 && bound_at(bd, w) == boundary(W, G, w), "bound_at w=%d", w);
+                CHECK(owner_b(bd, (int32_t)W, (int32_t)c_first) == wf && owner_b(bd, (int32_t)W, (int32_t)c_last) == wl,
+                      "owner_b w=%d", w);
+                const int32_t cp = (int32_t)pos.tile_cost0 + (int32_t)pos.stage * unit;
+                int gi = 0;
+                for (int j = 1; j < ng; ++j) gi += (int32_t)gs[j].cost_begin <= cp ? 1 : 0;
+                const Pos ph = locate<int32_t>(gs, ng, cp, gi);
+                CHECK(ph.group == p32.group && ph.nb == p32.nb && ph.mb == p32.mb && ph.stage == p32.stage &&
+                          ph.tile_cost0 == p32.tile_cost0, "locate from the counted group w=%d", w);
             }
             if (s_end < g.stages) break;
             pos = locate(gs, ng, pos.tile_cost0 + (int64_t)unit * g.stages);
@@ -132,6 +144,29 @@ static void run_launch(const std::vector<int>& M, const std::vector<int>& N, con
     run_case(M, N, K, cus, maxf, fmt);
 }
 
+// Division-free boundaries and owners against boundary() and owner() over
+// every workgroup count up to kMaxBoundsG, at random totals up to
+// kMaxLaunchCost and at the extremes.
+static void check_bounds()
+{
+    std::mt19937 brng(777);
+    for (int G = 1; G <= kMaxBoundsG; ++G) {
+        for (int rep = 0; rep < 4; ++rep) {
+            const int64_t W = rep == 0   ? kMaxLaunchCost
+                              : rep == 1 ? (int64_t)G * kMinUnitsPerWG
+                                         : 1 + (int64_t)(brng() % (uint32_t)kMaxLaunchCost);
+            const Bounds bd = make_bounds(W, G);
+            for (int w = 0; w <= G; ++w)
+                CHECK(bound_at(bd, w) == boundary(W, G, w), "bound_at G=%d W=%lld w=%d", G, (long long)W, w);
+            for (int k = 0; k < 16; ++k) {
+                const int32_t c = (int32_t)(brng() % (uint64_t)W);
+                CHECK(owner_b(bd, (int32_t)W, c) == owner(W, G, (int64_t)c), "owner_b G=%d W=%lld c=%d", G,
+                      (long long)W, c);
+            }
+        }
+    }
+}
+
 int main()
 {
     // The five workloads, at the size the host picks and at every size.
@@ -147,6 +182,7 @@ int main()
             run_launch(w[0], w[1], w[2], 256, fmt);
             for (int maxf = 1; maxf <= kMaxFrags; ++maxf) run_case(w[0], w[1], w[2], 256, maxf, fmt);
         }
+    check_bounds();
     // Random shapes, grid sizes and m-block sizes.
     std::mt19937 rng(12345);
     for (int it = 0; it < 3000; ++it) {
