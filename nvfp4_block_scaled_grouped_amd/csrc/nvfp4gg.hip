@@ -828,6 +828,11 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
             // the MFMAs of k-step v; the scheduling barrier at the end of each
             // k-step keeps the compiler from hoisting work across k-steps.
             h8_t bv[2] = {dequant8((uint32_t)bq[p][0][0], sbf[0][0]), dequant8((uint32_t)bq[p][1][0], sbf[1][0])};
+            // Raised priority from the first dequantised B piece to the
+            // barrier: a wave inside its k-steps issues ahead of one that is
+            // still waiting at the stage's start (measured: 12-fragment tiles
+            // about 5% faster, g8 K2048 N7168 about 2%).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int v = 0; v < kKSteps; ++v) {
                 h8_t av[NA];
@@ -878,6 +883,7 @@ __device__ __forceinline__ void run_segment(const LaunchArgs& args, const Pos& p
 #endif
                 __builtin_amdgcn_sched_barrier(0);
             }
+            __builtin_amdgcn_s_setprio(0);
             lds_barrier();
         };
 
