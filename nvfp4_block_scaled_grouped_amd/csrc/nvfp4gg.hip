@@ -917,39 +917,17 @@ __device__ __forceinline__ f4_t mfma_mx(i4_t b, uint32_t sb, i4_t a, uint32_t sa
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bv, av, c, 4, 4, 0, (int)sb, 0, (int)sa);
 }
 
-__device__ __forceinline__ uint32_t load_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
-{
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-}
-
-// Stages J .. R-1 of a ring pass: f(Parity<J>, i + J) for those below n.
-template <int J, int R, class F>
-__device__ __forceinline__ void ring_tail(F& f, int i, int n)
-{
-    if constexpr (J < R) {
-        if (i + J < n) {
-            f(Parity<J>{}, i + J);
-            ring_tail<J + 1, R>(f, i, n);
-        }
-    }
-}
-
-template <int J, int R, class F>
-__device__ __forceinline__ void ring_pass(F& f, int i)
-{
-    if constexpr (J < R) {
-        f(Parity<J>{}, i + J);
-        ring_pass<J + 1, R>(f, i);
-    }
-}
-
 // One segment of an MXFP4 tile (same tile shape, schedule, wave layout and
 // end of segment as run_segment):
 //   * B: each lane loads 16 bytes of its row per stage (the MFMA operand as
-//     it is) and its scale byte, kRing stages ahead in a register ring.
+//     it is), kRing stages ahead in a register ring.
 //   * A: wave w loads fragment w (and w + 8 for more than 8 fragments) the
 //     same way, one stage ahead of its use, and stores it with its scale
 //     bytes into a double-buffered LDS stage that every wave reads.
+//   * Scales: one 16-byte load per lane per block of 4 stages, staged
+//     through the wave's rows of LDS (a byte load per fragment and stage
+//     kept the texture address unit's queue full: measured 6x the full
+//     cycles of the NVFP4 kernel).
 //   * Per stage each wave runs 2 x NA MFMAs of 16 x 16 x 128; one LDS-only
 //     barrier ends the stage.
 template <int NA>
@@ -986,21 +964,30 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     const __amdgpu_buffer_rsrc_t rSB = make_rsrc(ga.SFB, (uint32_t)N * row_scales);
 
     // Rows past M or N are beyond the buffers and read zeros.
-    uint32_t offB[2], offSB[2];
+    uint32_t offB[2];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        const uint32_t brow = (uint32_t)(n0 + 32 * wave + 16 * f + c16);
-        offB[f] = brow * row_bytes + 16u * kq;
-        offSB[f] = brow * row_scales + (uint32_t)kq;
-    }
-    uint32_t offA[2], offSA[2];
+    for (int f = 0; f < 2; ++f) offB[f] = (uint32_t)(n0 + 32 * wave + 16 * f + c16) * row_bytes + 16u * kq;
+    uint32_t offA[2];
 #pragma unroll
-    for (int x = 0; x < kU; ++x) {
-        const int a = wave + kWaves * x;
-        const uint32_t arow = (uint32_t)(m0 + 16 * (a % NA) + c16);
-        offA[x] = arow * row_bytes + 16u * kq;
-        offSA[x] = arow * row_scales + (uint32_t)kq;
-    }
+    for (int x = 0; x < kU; ++x)
+        offA[x] = (uint32_t)(m0 + 16 * ((wave + kWaves * x) % NA) + c16) * row_bytes + 16u * kq;
+    // Scale staging, as in the NVFP4 kernel: lane L loads the 16 scale bytes
+    // (4 stages x 4) of one row for a block of 4 stages and writes them to
+    // row L of the wave's part of sm.sscr: rows 0..31 are the wave's B rows,
+    // rows 32 + 16 x .. its A unit x's rows (with one unit, lanes 48..63 load
+    // unit 0's rows again, into the same place).  Only the wave itself reads
+    // its rows, and a wave's LDS accesses complete in order, so no barrier
+    // guards them.  A block that runs past the end of K reads the next row's
+    // bytes or, past the buffer, zeros; the stages that would use them do not
+    // exist.  Lane (c16, kq) takes scale byte kq of its row's stage dword.
+    const bool sa_lane = lane >= 32;
+    const int sx = kU == 2 ? (lane >> 4) & 1 : 0;
+    const int srow = sa_lane ? 32 + 16 * sx + (lane & 15) : lane;
+    const uint32_t offS =
+        (sa_lane ? (uint32_t)(m0 + 16 * ((wave + kWaves * sx) % NA) + (lane & 15)) : (uint32_t)(n0 + 32 * wave + lane)) *
+        row_scales;
+    const __amdgpu_buffer_rsrc_t rS = sa_lane ? rSA : rSB;
+    const uint32_t kshift = 8u * (uint32_t)kq;
 
     f4_t acc[NA][2];
 #pragma unroll
@@ -1010,13 +997,10 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
 
     {
         const int n = s_end - s_begin;
-        // Stage offsets in a row of codes and of scales; stages past the
-        // chain repeat its last stage (loaded, never used).
+        // Stage offsets in a row of codes; stages past the chain repeat its
+        // last stage (loaded, never used).
         auto sbyte = [&](int t) {
             return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 2));
-        };
-        auto sscl = [&](int t) {
-            return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + (t < n ? t : n - 1)) * (kStageK / 32));
         };
         // A stores of waves whose unit is past the tile's fragments go to a
         // discard area, so the stage has no branch (a branch would let the
@@ -1038,39 +1022,57 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
             *reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(sdst[x]) + buf * mstep[x]) = sc;
         };
 
+        // The scale block starting at stage b of the chain (4 bytes per stage),
+        // in the per-lane offset, which the buffer's range check covers.
+        auto sblock = [&](int b) { return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (kStageK / 32)); };
+        i4_t sreg;
+        auto scale_load = [&](int b) {
+            sreg = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(rS, offS + sblock(b), 0, 0));
+        };
+        auto scale_store = [&](int buf) { *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][srow][0]) = sreg; };
+        // The E8M0 byte of this lane for stage t of the chain: B fragment f,
+        // or A unit x (the MFMA reads byte 0 of the scale operand).
+        auto scale_b = [&](int t, int f) { return sm.sscr[(t >> 2) & 1][wave][16 * f + c16][t & 3] >> kshift; };
+        auto scale_a = [&](int t, int x) { return sm.sscr[(t >> 2) & 1][wave][32 + 16 * x + c16][t & 3] >> kshift; };
+
         i4_t bq[kRing][2], aq[kRing][2];
-        uint32_t bs[kRing][2], as[kRing][2];
         {
             i4_t a0[2];
-            uint32_t s0[2];
+            scale_load(0);
 #pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                a0[x] = load16(rA, offA[x], sbyte(0));
-                s0[x] = load_u8(rSA, offSA[x], sscl(0));
-            }
+            for (int x = 0; x < kU; ++x) a0[x] = load16(rA, offA[x], sbyte(0));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kRing; ++j) {
 #pragma unroll
-                for (int f = 0; f < 2; ++f) {
-                    bq[j][f] = load16(rB, offB[f], sbyte(j));
-                    bs[j][f] = load_u8(rSB, offSB[f], sscl(j));
-                }
+                for (int f = 0; f < 2; ++f) bq[j][f] = load16(rB, offB[f], sbyte(j));
 #pragma unroll
-                for (int x = 0; x < kU; ++x) {
-                    aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
-                    as[j][x] = load_u8(rSA, offSA[x], sscl(j + 1));
-                }
+                for (int x = 0; x < kU; ++x) aq[j][x] = load16(rA, offA[x], sbyte(j + 1));
                 __builtin_amdgcn_sched_barrier(0);
             }
+            scale_store(0);
 #pragma unroll
-            for (int x = 0; x < kU; ++x) put_a(0, x, a0[x], s0[x]);
+            for (int x = 0; x < kU; ++x) put_a(0, x, a0[x], scale_a(0, x));
         }
         lds_barrier();
 
-        auto stage = [&](auto parity, int i) {
+        // Stage i of the chain at ring slot p = i % kRing and scale-block phase
+        // q = i % 4, both known at compile time (the loop is unrolled by 4).
+        auto stage = [&](auto parity, auto phase, int i) {
             constexpr int p = decltype(parity)::value;
+            constexpr int q = decltype(phase)::value;
             const int lb = i & 1;
+            const uint32_t sbv[2] = {scale_b(i, 0), scale_b(i, 1)};
+            // The A scale of stage i + 1 (or this one past the chain's end).
+            const int ia = i + 1 < n ? i + 1 : i;
+            uint32_t sav[2];
+#pragma unroll
+            for (int x = 0; x < kU; ++x) sav[x] = scale_a(ia, x);
+            // Block b + 1's scales go out at the first stage of block b and
+            // are staged at its third stage, before the A of its last stage
+            // needs them.
+            if constexpr (q == 0) scale_load(i + 4);
+            if constexpr (q == 2) scale_store(((i >> 2) + 1) & 1);
 #pragma unroll
             for (int a0 = 0; a0 < NA; a0 += kAGroup) {
 #pragma unroll
@@ -1078,7 +1080,7 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
                     const i4_t av = sm.mx[lb].v[a][lane];
                     const uint32_t sa = sm.mx[lb].s[a][lane];
 #pragma unroll
-                    for (int f = 0; f < 2; ++f) acc[a][f] = mfma_mx(bq[p][f], bs[p][f], av, sa, acc[a][f]);
+                    for (int f = 0; f < 2; ++f) acc[a][f] = mfma_mx(bq[p][f], sbv[f], av, sa, acc[a][f]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -1086,36 +1088,24 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
             // i - 1 passed the previous barrier), then the ring slot's
             // reloads: B of stage i + kRing, A of stage i + 1 + kRing.
 #pragma unroll
-            for (int x = 0; x < kU; ++x) put_a(lb ^ 1, x, aq[p][x], as[p][x]);
+            for (int x = 0; x < kU; ++x) put_a(lb ^ 1, x, aq[p][x], sav[x]);
             // The slot's old values are consumed before its reloads are
             // issued, so the reloads can take the same registers (otherwise
             // the compiler copies ring values whose loads are in flight and
             // waits for them).
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                fence_after(bq[p][f]);
-                fence_after(bs[p][f]);
-            }
+            for (int f = 0; f < 2; ++f) fence_after(bq[p][f]);
 #pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                fence_after(aq[p][x]);
-                fence_after(as[p][x]);
-            }
+            for (int x = 0; x < kU; ++x) fence_after(aq[p][x]);
 #pragma unroll
-            for (int f = 0; f < 2; ++f) {
-                bq[p][f] = load16(rB, offB[f], sbyte(i + kRing));
-                bs[p][f] = load_u8(rSB, offSB[f], sscl(i + kRing));
-            }
+            for (int f = 0; f < 2; ++f) bq[p][f] = load16(rB, offB[f], sbyte(i + kRing));
 #pragma unroll
-            for (int x = 0; x < kU; ++x) {
-                aq[p][x] = load16(rA, offA[x], sbyte(i + 1 + kRing));
-                as[p][x] = load_u8(rSA, offSA[x], sscl(i + 1 + kRing));
-            }
+            for (int x = 0; x < kU; ++x) aq[p][x] = load16(rA, offA[x], sbyte(i + 1 + kRing));
             lds_barrier();
         };
         int i = 0;
-        for (; i + kRing - 1 < n; i += kRing) ring_pass<0, kRing>(stage, i);
-        ring_tail<0, kRing>(stage, i, n);
+        for (; i + 3 < n; i += 4) phase_pass<0, 4, kRing>(stage, i);
+        phase_tail<0, 4, kRing>(stage, i, n);
     }
     finish_segment<NA>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
