@@ -101,9 +101,12 @@ NVFP4_HD GroupSched make_group_sched(int M, int N, int K, int64_t cost_begin, in
 // Cost of one stage of a tile with f = 1..kMaxFrags fragments, in units of
 // about 50 ns.  NVFP4: measured MI355X stage times 1.2, 1.45, 1.75, 2.3 and
 // 2.8 us for 4, 6, 8, 10 and 12 fragments; odd counts interpolated (the
-// MFMAs grow linearly with f), 1 and 2 extrapolated.  MXFP4: measured 1.15,
-// 1.25, 1.3 and 1.8 us for 4, 6, 8 and 10-12 fragments (the step at 9:
-// every wave then stages a second A fragment).
+// MFMAs grow linearly with f), 1 and 2 extrapolated.  MXFP4 (scales staged
+// in 4-stage blocks): one tile per workgroup at K 7168 and K 3584 gives
+// 1.01, 1.07, 1.16, 1.12, 1.17, 1.22, 1.23, 1.18, 1.47, 1.54, 1.52 and
+// 1.66 us per stage for 1..12 fragments, taken monotone in units of the
+// NVFP4 table's 1-fragment stage (the step at 9: every wave then stages a
+// second A fragment).
 NVFP4_HD int tile_cost(int f) { return kTileCostBase + kTileCostPerFrag * f; }
 
 NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
@@ -114,9 +117,9 @@ NVFP4_HD int unit_cost(int f, int fmt = kFmtNvfp4)
     // chain of branches (measured: about 2 us per walk).
     //            f =   8  7  6  5  4  3  2  1                 12 11 10  9
     // NVFP4:          35 32 29 27 24 23 21 20                 56 51 46 41
-    // MXFP4:          26 26 25 24 23 23 22 22                 36 36 36 36
+    // MXFP4:          23 23 22 22 21 21 20 19                 31 29 28 27
     const bool mx = fmt == kFmtMxfp4;
-    const uint64_t word = f <= 8 ? (mx ? 0x1a1a191817171616ull : 0x23201d1b18171514ull) : (mx ? 0x0000000024242424ull : 0x0000000038332e29ull);
+    const uint64_t word = f <= 8 ? (mx ? 0x1717161615151413ull : 0x23201d1b18171514ull) : (mx ? 0x000000001f1d1c1bull : 0x0000000038332e29ull);
     const int i = (f <= 1 ? 0 : f > kMaxFrags ? kMaxFrags - 1 : f - 1) & 7;
     return (int)((word >> (8 * i)) & 0xFF);
 }
