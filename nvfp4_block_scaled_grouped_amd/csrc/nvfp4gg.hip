@@ -1110,8 +1110,8 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     finish_segment<NA>(args, pos, first_chain, last_chain, sm, s_flag, acc, m0, n0, wave);
 }
 
-// Wave-uniform values computed in vector registers (64-bit divisions have
-// no scalar form) moved back to scalar registers, so they do not occupy
+// Wave-uniform values computed in vector registers (divisions and LDS reads
+// have no scalar form) moved back to scalar registers, so they do not occupy
 // vector registers through the whole loop.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int64_t uniform(int64_t v)
@@ -1184,10 +1184,11 @@ __device__ __forceinline__ void walk_step(const LaunchArgs& args, const GroupSch
 // (a tile's stages in the range) as chains of at most kMaxChainStages
 // stages, each by the segment kernel of its fragment count.
 //
-// The walk's 64-bit cost arithmetic runs on the scalar unit, which all
-// waves of a CU share: done by every wave it took about 3 us per segment
-// (measured), so wave 0 alone computes each segment (its position, its end,
-// the tile's first and last contributors) and publishes it in sm.walk.
+// The walk's arithmetic runs largely on the scalar unit, which all waves of
+// a CU share: done by every wave it took about 3 us per segment (measured,
+// with 64-bit costs), so wave 0 alone computes each segment (its position,
+// its end, the tile's first and last contributors) and publishes it in
+// sm.walk.
 template <bool kMx, bool kBlocked>
 __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm, int* s_flag)
 {
@@ -1195,6 +1196,7 @@ __device__ __forceinline__ void walk_range(const LaunchArgs& args, SharedMem& sm
     // kMaxLaunchCost).  Wave 0's walk state (the next position and the
     // range's end) lives in LDS between segments, so no register holds it
     // through a segment.
+    //
     // The group table goes to LDS with one 16-byte load per lane, issued
     // before anything waits for the scalar loads of W and G: its lines then
     // arrive in the same memory round trip as those, where the walk's scan of
