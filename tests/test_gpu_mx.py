@@ -85,3 +85,26 @@ def test_mx_many_groups(nv, oracle_lib):
     C = _run(nv, M, N, K, A, B, SA, SB)
     for i in range(g):
         _compare.assert_close(C[i], C_ref[i], X[i], "group %d" % i)
+
+
+def test_mx_long_segments_run_as_several_chains(nv, oracle_lib):
+    """K = 17408 (136 stages of 128) over 128 column blocks, as the NVFP4
+    chain test: a workgroup's segment runs as several chains, each restarting
+    the scale blocks at its first stage.  Checked on sampled elements
+    (corners, centre and random points) against the oracle's one-element
+    form."""
+    M, N, K = [96], [32768], [17408]
+    _say("mx long segments M=%s N=%s K=%s" % (M, N, K))
+    A, B, SA, SB = workloads.make_mx_inputs(M, N, K, 63)
+    C = _run(nv, M, N, K, A, B, SA, SB)[0]
+    assert not np.isnan(C.astype(np.float32)).any()
+    rng = np.random.default_rng(8)
+    pts = {(m, n) for m in (0, M[0] // 2, M[0] - 1) for n in (0, N[0] // 2, N[0] - 1)}
+    pts |= {(int(m), int(n)) for m, n in zip(rng.integers(0, M[0], 300), rng.integers(0, N[0], 300))}
+    y, r, x = [], [], []
+    for m, n in sorted(pts):
+        c16, ex = oracle_lib.mx_gemm_element(M[0], N[0], K[0], A[0], B[0], SA[0], SB[0], m, n)
+        y.append(C[m, n])
+        r.append(np.uint16(c16).view(np.float16))
+        x.append(ex)
+    _compare.assert_close(np.array(y), np.array(r), np.array(x), "mx long segments")
