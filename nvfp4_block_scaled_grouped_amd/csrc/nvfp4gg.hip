@@ -980,13 +980,15 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
     // guards them.  A block that runs past the end of K reads the next row's
     // bytes or, past the buffer, zeros; the stages that would use them do not
     // exist.  Lane (c16, kq) takes scale byte kq of its row's stage dword.
+    // Every lane issues the block's load from both scale arrays, the one it
+    // does not use at an offset past the array (which reads zeros), so each
+    // load's buffer descriptor is the same for the whole wave.
     const bool sa_lane = lane >= 32;
     const int sx = kU == 2 ? (lane >> 4) & 1 : 0;
     const int srow = sa_lane ? 32 + 16 * sx + (lane & 15) : lane;
-    const uint32_t offS =
-        (sa_lane ? (uint32_t)(m0 + 16 * ((wave + kWaves * sx) % NA) + (lane & 15)) : (uint32_t)(n0 + 32 * wave + lane)) *
-        row_scales;
-    const __amdgpu_buffer_rsrc_t rS = sa_lane ? rSA : rSB;
+    const uint32_t offSBl = sa_lane ? kNoSlot : (uint32_t)(n0 + 32 * wave + lane) * row_scales;
+    const uint32_t offSAl =
+        sa_lane ? (uint32_t)(m0 + 16 * ((wave + kWaves * sx) % NA) + (lane & 15)) * row_scales : kNoSlot;
     const uint32_t kshift = 8u * (uint32_t)kq;
 
     f4_t acc[NA][2];
@@ -1025,11 +1027,18 @@ __device__ __forceinline__ void run_segment_mx(const LaunchArgs& args, const Pos
         // The scale block starting at stage b of the chain (4 bytes per stage),
         // in the per-lane offset, which the buffer's range check covers.
         auto sblock = [&](int b) { return (uint32_t)__builtin_amdgcn_readfirstlane((s_begin + b) * (kStageK / 32)); };
-        i4_t sreg;
+        // The two halves are combined only where the block is staged, so the
+        // loads are waited for there (combined at the load, the wait would
+        // drain every load in flight).
+        i4_t sregB, sregA;
         auto scale_load = [&](int b) {
-            sreg = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(rS, offS + sblock(b), 0, 0));
+            const uint32_t sb = sblock(b);
+            sregB = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(rSB, offSBl + sb, 0, 0));
+            sregA = __builtin_bit_cast(i4_t, __builtin_amdgcn_raw_buffer_load_b128(rSA, offSAl + sb, 0, 0));
         };
-        auto scale_store = [&](int buf) { *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][srow][0]) = sreg; };
+        auto scale_store = [&](int buf) {
+            *reinterpret_cast<i4_t*>(&sm.sscr[buf][wave][srow][0]) = sregB | sregA;
+        };
         // The E8M0 byte of this lane for stage t of the chain: B fragment f,
         // or A unit x (the MFMA reads byte 0 of the scale operand).
         auto scale_b = [&](int t, int f) { return sm.sscr[(t >> 2) & 1][wave][16 * f + c16][t & 3] >> kshift; };
