@@ -48,7 +48,10 @@
  *                            device pointer of a non-empty operand
  *   NVFP4GG_UNSUPPORTED  -2  valid but outside what the kernels handle: a
  *                            non-empty group with K_i % 128 != 0, an operand
- *                            of 2 GiB or more, or M_i * N_i >= 2^31
+ *                            of 2 GiB or more, M_i * N_i >= 2^31, a launch
+ *                            whose schedule cost reaches 2^31 units (over
+ *                            100 s of GPU work), or a grid of more than 1024
+ *                            workgroups (a device with more compute units)
  *   NVFP4GG_HIP_ERROR    -3  a HIP call (launch, first-call workspace allocation) failed
  * nvfp4_group_gemm_last_error() describes the last failure on this thread.
  */
